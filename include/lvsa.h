@@ -1,0 +1,167 @@
+/*
+ * lvsa.h -- C ABI of the MI355X (gfx950) LVSA frame-block-sparse attention.
+ *
+ * LVSA ("LVSA: Training-Free Sparse Attention for Long Video Diffusion";
+ * gist.science explainer, Technical Summary §2 "Core Mechanism") restricts
+ * every latent query frame t of a video diffusion transformer to a key-frame
+ * set A(t) = G_s ∪ W(t): rotating global anchor frames G_s plus an expanded
+ * local window W(t), with |A(t)| held at a budget C.  The mask is rebuilt on
+ * the host every denoising step (TechWalker article on LVSA, §二 and §三) and
+ * the attention runs only over the frame blocks it lists.
+ *
+ * Conventions for every call:
+ *   - Return value: LVSA_OK (0) or a negative LVSA_ERR_* code.  A readable
+ *     message for the last failure on the calling thread is returned by
+ *     lvsa_last_error().
+ *   - Ownership: the caller owns every buffer, host and device.  The library
+ *     allocates no device memory, frees nothing, keeps no pointer after the
+ *     call returns, and never synchronises a stream.
+ *   - Thread safety: all calls are reentrant; error messages are per thread.
+ */
+#ifndef LVSA_H_
+#define LVSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LVSA_ABI_VERSION 1
+
+/* Status codes. */
+#define LVSA_OK            0
+#define LVSA_ERR_ARG      -1 /* argument out of domain or null pointer           */
+#define LVSA_ERR_CAPACITY -2 /* caller buffer smaller than the required size     */
+#define LVSA_ERR_SHAPE    -3 /* tensor shapes/strides/alignment not supported    */
+#define LVSA_ERR_DTYPE    -4 /* element type not supported (bf16 only)           */
+#define LVSA_ERR_HIP      -5 /* no gfx950 device, or a HIP launch error          */
+#define LVSA_ERR_MASK     -6 /* CSR mask malformed                               */
+
+/* Anchor rotation flags for lvsa_build_mask.
+ *   LVSA_ROT_MOD_TPER (default): anchor offset o_s = step mod Tper, the shift
+ *     the gist.science explainer prints (Technical Summary §2, "Rotating
+ *     Global Anchors": G_s shifts by s mod Tper).
+ *   LVSA_ROT_MOD_T: o_s = step mod T, anchors advancing one frame per step
+ *     cyclically over the frame count (TechWalker article, §三).  Identical
+ *     to the default whenever Tper divides T.
+ *   LVSA_FIXED_GRID: o_s = 0 at every step, the non-rotating grid the pages
+ *     describe as the cause of fixed-grid bias (ablation). */
+#define LVSA_ROT_MOD_TPER 0
+#define LVSA_ROT_MOD_T    1
+#define LVSA_FIXED_GRID   2
+
+/* Element types. */
+#define LVSA_DTYPE_BF16 1
+
+/* What lvsa_build_mask derived for the step. */
+typedef struct lvsa_mask_info {
+  int32_t c_eff;    /* min(C, T): key frames per query frame                  */
+  int32_t t_per;    /* anchor spacing Tper = ceil(T/(C-W)); 0 when T <= C     */
+  int32_t n_anchor; /* anchor count n_g = ceil(T/Tper); 0 when T <= C         */
+  int32_t offset;   /* anchor offset o_s used at this step; 0 when T <= C     */
+  int32_t nnz;      /* T * c_eff entries written to col_idx                   */
+} lvsa_mask_info;
+
+/* A 4-D tensor [B, H, N, D] in device memory, D contiguous (stride 1).
+ * Strides are in elements.  N is the token count T*P, token index t*P + p
+ * (frame-major).  data must be 16-byte aligned and stride_b, stride_h,
+ * stride_n multiples of 8 elements (16 bytes). */
+typedef struct lvsa_tensor {
+  void *data;
+  int64_t B, H, N, D;
+  int64_t stride_b, stride_h, stride_n;
+  int32_t dtype; /* LVSA_DTYPE_BF16 */
+} lvsa_tensor;
+
+/* ABI version (LVSA_ABI_VERSION). */
+int lvsa_version(void);
+
+/* Message describing the last failure on this thread ("" if none).  The
+ * string is owned by the library and valid until the next call on this
+ * thread. */
+const char *lvsa_last_error(void);
+
+/* Number of col_idx entries lvsa_build_mask writes for (T, C, W):
+ * T * min(C, T).  Same argument domain as lvsa_build_mask (step and flags
+ * do not change the size).  Errors: LVSA_ERR_ARG. */
+int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out);
+
+/* Host mask builder: the key frames of every query frame at one denoising
+ * step, as CSR.
+ *
+ * Source: gist.science explainer, Technical Summary §2 "Core Mechanism"
+ * (A(t) = G ∪ W(t); rotating periodic anchors; window extended over anchors
+ * so |A(t)| stays at the budget C); TechWalker article §二 (C = training
+ * horizon in latent frames; Tper ≈ T/(C−W); extension on the CPU) and §三
+ * (rotation; constant anchor count; each frame an anchor once per period).
+ *
+ * Definition (readings of the pages where they leave a step open):
+ *   T <= C : every row is 0..T-1 (dense; at the training horizon the method
+ *            is the dense model).
+ *   T >  C : Tper = ceil(T/(C-W)), n_g = ceil(T/Tper),
+ *            G = { (o_s + k*Tper) mod T : 0 <= k < n_g }, o_s per flags;
+ *            W(t) = the C - n_g non-anchor frames nearest to t, ties to the
+ *            lower frame index (so the window slides inward at the ends and
+ *            grows past anchors it overlaps);
+ *            A(t) = G ∪ W(t), |A(t)| = C.
+ *
+ * Arguments (all host memory, caller-owned):
+ *   T >= 1 frames, C >= 2 budget, 1 <= W <= C-1 window, step >= 0, flags one
+ *   of LVSA_ROT_MOD_TPER / LVSA_ROT_MOD_T / LVSA_FIXED_GRID.
+ *   row_ptr [T+1] out: row_ptr[t] = t * c_eff.
+ *   col_idx [cap] out: rows concatenated, each ascending and unique.
+ *   info    out, may be NULL.
+ * Errors: LVSA_ERR_ARG (domain, null row_ptr/col_idx), LVSA_ERR_CAPACITY
+ *   (cap < T * min(C,T)); on error nothing is written. */
+int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags,
+                    int32_t *row_ptr, int32_t *col_idx, int32_t cap,
+                    lvsa_mask_info *info);
+
+/* Host check of a CSR frame mask (any source): row_ptr[0] == 0,
+ * non-decreasing, row_ptr[T] == nnz, every row non-empty, ascending, unique
+ * and within [0, T).  Errors: LVSA_ERR_ARG (null/negative sizes),
+ * LVSA_ERR_MASK (the first violation, described by lvsa_last_error()). */
+int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx,
+                       int32_t nnz);
+
+/* Frame-block-sparse attention on the GPU.
+ *
+ * Source: gist.science explainer, Technical Summary §2 ("Core Mechanism":
+ * query frame t attends to the frames of A(t) only; "Complexity": per query
+ * O(C·P·d), so the sparsity block is the frame).  For every (b, h) and query
+ * token i of frame t = i / P:
+ *   out[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:]·k[b,h,j,:]) v[b,h,j,:]
+ * over the key tokens j of the frames in A(t) (non-causal, no bias).
+ * Arithmetic: bf16 products on the matrix cores with fp32 accumulation, fp32
+ * online softmax, probabilities rounded to bf16 for the P·V product, output
+ * rounded to bf16 (nearest-even).
+ *
+ * Arguments:
+ *   q, k, v, out : [B, H, N, D] bf16 device tensors, identical B/H/N/D,
+ *                  D in {64, 128}, N = T * P; out must not overlap q/k/v.
+ *   row_ptr_dev  : [T+1] int32 device array, CSR row offsets into col_idx.
+ *   col_idx_dev  : [nnz] int32 device array, key frames of each query frame,
+ *                  ascending and unique per row (lvsa_build_mask's output
+ *                  copied to the device).  Entries outside [0, T) are
+ *                  skipped and offsets are clamped to [0, nnz], so a
+ *                  malformed mask gives wrong numbers, never an
+ *                  out-of-bounds access; a row with no valid frame yields
+ *                  zeros.
+ *   T            : frames (N % T must be 0).
+ *   nnz          : length of col_idx_dev.
+ *   scale        : softmax scale; <= 0 selects 1/sqrt(D).
+ *   stream       : hipStream_t to launch on (NULL = default stream).
+ * The call is asynchronous on `stream`.  Argument errors are reported
+ * synchronously and launch nothing.  Errors: LVSA_ERR_ARG, LVSA_ERR_SHAPE,
+ * LVSA_ERR_DTYPE, LVSA_ERR_HIP (no gfx950 device current, launch failure). */
+int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                   const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                   int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LVSA_H_ */
