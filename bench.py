@@ -1,0 +1,242 @@
+"""Benchmark of the LVSA hot path on one MI355X.
+
+One step = one denoising step of the attention hot path over the whole
+workload: build the step's CSR mask on the host (C++), copy it to the device,
+run the frame-block-sparse attention kernel on [B, H, T·P, d] bf16.  The
+workload is the Wan-2.1-1.3B-shaped 6× horizon: B=1, H=12, d=128, T=121
+latent frames × 1560 tokens (480×832 video), C=21, W=9, anchors rotating
+with the step (seeded synthetic N(0,1) inputs, resident in HBM before the
+timed region).
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value      effective TFLOP/s = algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d per
+             step ÷ time per step (padding and softmax not counted)
+  roofline   for the attention kernel, from HIP events around each launch
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same step
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan13b_6x]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+PEAK_HBM_GBS = 8000.0
+METRIC = "LVSA attention effective TFLOP/s + ms/call, T=121×1560 tok, H=12 d=128 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_wan13b_6x.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_lvsa_amd", "csrc", "attention.hip")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(w) -> float:
+    return 4.0 * w.B * w.H * w.T * min(w.C, w.T) * w.P * w.P * w.D
+
+
+def measured_traffic(w, n_launch_units: float):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
+    when it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != w.name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The float64 oracle on a bounded sample: query frames of head 0 at step
+    0, taken in order until ``budget_s`` of CPU time is used."""
+    import torch
+    import oracle
+
+    rows = oracle.key_frames(w.T, w.C, w.W, 0)
+    qh, kh, vh = (x[:, :1].cpu() for x in (q, k, v))
+    threads = torch.get_num_threads()
+    per_frame = 4.0 * min(w.C, w.T) * w.P * w.P * w.D
+    done = 0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < budget_s:
+        oracle.block_attention(qh, kh, vh, rows, frames=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": per_frame * done / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{w.name}: head 0, step 0, query frames 0..{done - 1} ({done} of {w.T} frames × {w.H} heads), "
+                  f"float64 torch-CPU, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_6x")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_lvsa_amd as L
+    from block_sparse_attention_lvsa_amd.synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    lib = L.library()
+    log(f"workload {w}")
+    q, k, v = make_qkv(w, device=dev)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    T, C, W = w.T, w.C, w.W
+    nnz = L.lvsa_mask_nnz(T, C, W)
+    total = args.warmup + args.steps
+    # One pinned host buffer pair per step (the host never rewrites a buffer
+    # whose copy may still be pending) and one device pair (same stream, so
+    # copy s+1 runs after kernel s).
+    h_rp = [torch.empty(T + 1, dtype=torch.int32, pin_memory=True) for _ in range(total)]
+    h_ci = [torch.empty(nnz, dtype=torch.int32, pin_memory=True) for _ in range(total)]
+    d_rp = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    d_ci = torch.empty(nnz, dtype=torch.int32, device=dev)
+    info = L.LvsaMaskInfo()
+    recs = [L._tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+
+    def step(i: int, s: int, ev=None, mask_times=None):
+        t0 = time.perf_counter()
+        rc = lib.lvsa_build_mask(T, C, W, s, L.LVSA_ROT_MOD_TPER,
+                                 ctypes.cast(ctypes.c_void_p(h_rp[i].data_ptr()), I32P),
+                                 ctypes.cast(ctypes.c_void_p(h_ci[i].data_ptr()), I32P), nnz, ctypes.byref(info))
+        if mask_times is not None:
+            mask_times.append(time.perf_counter() - t0)
+        if rc:
+            raise RuntimeError(L.lvsa_last_error())
+        d_rp.copy_(h_rp[i], non_blocking=True)
+        d_ci.copy_(h_ci[i], non_blocking=True)
+        if ev is not None:
+            ev[0].record(stream)
+        rc = lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
+                                ctypes.c_void_p(d_rp.data_ptr()), ctypes.c_void_p(d_ci.data_ptr()),
+                                T, nnz, ctypes.byref(recs[3]), 0.0, sp)
+        if ev is not None:
+            ev[1].record(stream)
+        if rc:
+            raise RuntimeError(L.lvsa_last_error())
+
+    for i in range(args.warmup):
+        step(i, i)
+    torch.cuda.synchronize()
+
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    mask_times = []
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    g0.record(stream)
+    for j in range(args.steps):
+        step(args.warmup + j, j, kev[j], mask_times)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = g0.elapsed_time(g1)
+    ms_per_step = max(total_ms, wall * 1e3) / args.steps
+    kms = sorted(a.elapsed_time(b) for a, b in kev)
+    k_avg = sum(kms) / len(kms)
+    flops = algorithmic_flops(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    log(f"step: {ms_per_step:.3f} ms  kernel avg {k_avg:.3f} ms (p10 {kms[len(kms) // 10]:.3f}, "
+        f"p90 {kms[(9 * len(kms)) // 10]:.3f})  {value:.1f} TFLOP/s effective, kernel {achieved:.1f} TFLOP/s")
+    log(f"host mask build: median {sorted(mask_times)[len(mask_times) // 2] * 1e6:.1f} us/step")
+
+    extra = {}
+    if not args.no_dense:
+        # Dense comparator: the same kernel with a C = T mask (one run of N keys).
+        dm = L.lvsa_build_mask(T, max(T, 2), 1, 0)
+        if True:
+            dmd = dm.to(dev)
+            reps = 3
+            L.lvsa_attention(q, k, v, dmd, out=out)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                L.lvsa_attention(q, k, v, dmd, out=out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dense_ms = e0.elapsed_time(e1) / reps
+            extra = {"dense_ms_per_call": round(dense_ms, 3),
+                     "speedup_vs_dense_kernel": round(dense_ms / k_avg, 3),
+                     "ideal_speedup_T_over_C": round(T / min(C, T), 3)}
+            log(f"dense (C=T) kernel: {dense_ms:.3f} ms -> speedup {dense_ms / k_avg:.2f}x (ideal {T / min(C, T):.2f}x)")
+
+    traffic = measured_traffic(w, 1)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+            "kernel": "lvsa_attn_fwd<128,4>", "kernel_ms_avg": round(k_avg, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
+        log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "P": w.P, "d": w.D, "C": w.C, "W": w.W,
+                   "tokens": w.N, "rotation": "mod_tper", "denoising_steps": f"0..{args.steps - 1}",
+                   "flops_per_step": flops, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        **extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

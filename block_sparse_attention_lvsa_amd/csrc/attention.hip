@@ -83,7 +83,7 @@ struct RunIter {
       const int32_t f = cols[e++];
       if (f < 0 || f >= T) continue;  // malformed entry: skipped, never read
       int32_t f1 = f;
-      while (e < e_end && cols[e] == f1 + 1) { ++f1; ++e; }
+      while (e < e_end && f1 + 1 < T && cols[e] == f1 + 1) { ++f1; ++e; }
       ks = f * P;
       ke = (f1 + 1) * P;
       return true;

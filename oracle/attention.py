@@ -59,11 +59,13 @@ def _softmax_weighted_sum(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
 
 def block_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     rows: List[List[int]], scale: Optional[float] = None,
-                    q_chunk: int = 256) -> torch.Tensor:
+                    q_chunk: int = 256, frames: Optional[Sequence[int]] = None) -> torch.Tensor:
     """Full output [B, H, N, d] float64 of frame-block-sparse attention.
 
     q, k, v: [B, H, N, d] (any float dtype; bf16 is up-cast exactly).
     rows:    rows[t] = A(t), the key frames of query frame t (len T).
+    frames:  if given, only these query frames are computed (the other
+             output rows are left NaN) -- for bounded samples of large cases.
     """
     q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
     B, H, N, d = q64.shape
@@ -72,11 +74,12 @@ def block_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("N must be a multiple of T")
     P = N // T
     sc = default_scale(d) if scale is None else float(scale)
-    out = torch.empty_like(q64)
+    out = torch.full_like(q64, float("nan"))
     tok = [_frame_tokens(r, P) for r in rows]
+    todo = range(T) if frames is None else list(frames)
     for b in range(B):
         for h in range(H):
-            for t in range(T):
+            for t in todo:
                 K_A = k64[b, h, tok[t]]
                 V_A = v64[b, h, tok[t]]
                 for c0 in range(0, P, q_chunk):

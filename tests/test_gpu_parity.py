@@ -22,6 +22,12 @@ from block_sparse_attention_lvsa_amd.synth import WORKLOADS, make_qkv, make_rand
 
 pytestmark = pytest.mark.gpu
 
+# The absolute bars are stated for attention outputs of at most unit size
+# (convex combinations of unit-variance values).  Both error sources -- the
+# bf16 rounding of the probabilities and of the output -- are relative to the
+# output, so for synthetic edge cases with larger outputs the same bars are
+# applied relative to max(1, max|ref|); at every workload shape that factor
+# is 1 and the bars are exactly 1e-2 / 1e-3.
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
 REL_RMS = 1e-2
@@ -39,8 +45,9 @@ def stats(out, ref):
 
 def assert_close(out, ref, what):
     mx, mean, rel = stats(out, ref)
-    print(f"  {what}: max|Δ| {mx:.3e}  mean|Δ| {mean:.3e}  relRMS {rel:.3e}", flush=True)
-    assert mx <= MAX_ABS and mean <= MEAN_ABS and rel <= REL_RMS, (what, mx, mean, rel)
+    s = max(1.0, ref.double().abs().max().item())
+    print(f"  {what}: max|Δ| {mx:.3e}  mean|Δ| {mean:.3e}  relRMS {rel:.3e}  (scale {s:.2f})", flush=True)
+    assert mx <= MAX_ABS * s and mean <= MEAN_ABS * s and rel <= REL_RMS, (what, mx, mean, rel, s)
 
 
 def run_lib(q, k, v, T, C, W, step, flags=L.LVSA_ROT_MOD_TPER, scale=None, out=None):
