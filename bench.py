@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -118,6 +120,15 @@ def main():
     q, k, v = make_qkv(w, device=dev)
     out = torch.empty_like(q)
     torch.cuda.synchronize()
+    if args.calib_copy:
+        # Reads exactly 2^30 bytes and writes 2^30 bytes per launch: the
+        # reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings.
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     T, C, W = w.T, w.C, w.W
     nnz = L.lvsa_mask_nnz(T, C, W)

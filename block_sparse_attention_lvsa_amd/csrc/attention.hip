@@ -52,20 +52,31 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-constexpr int kBN = 64;             // keys per LDS tile
+// Tuning knobs (compile-time): waves per workgroup and the register budget
+// expressed as resident waves per SIMD.
+#ifndef LVSA_NW
+#define LVSA_NW 4
+#endif
+#ifndef LVSA_WAVES_PER_SIMD
+#define LVSA_WAVES_PER_SIMD 2
+#endif
+#ifndef LVSA_BN
+#define LVSA_BN 64
+#endif
+
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
 
 struct Args {
   const u16 *q, *k, *v;
   u16 *o;
-  int64_t q_sb, q_sh, q_sn;
-  int64_t k_sb, k_sh, k_sn;
-  int64_t v_sb, v_sh, v_sn;
-  int64_t o_sb, o_sh, o_sn;
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int32_t q_sn, k_sn, v_sn, o_sn;  // token strides (elements; < 2^24)
   const int32_t *row_ptr, *col_idx;
   int32_t nnz, T, P, H, q_tiles, n_wg;
   float scale_log2;  // softmax scale × log2(e)
@@ -103,36 +114,226 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// Packs the low (hi=false) or high (hi=true) bf16 halves of two words.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
-
+// LDS tile layout.  K and V tiles are kept in their natural [key][d] order
+// (one 2·D-byte row per key), filled straight from global memory by
+// global_load_lds (16 bytes per lane, 1 KB per wave instruction), with the
+// 16-byte chunks of each row XOR-swizzled by key so that the MFMA operand
+// reads are bank-conflict free:
+//   K: chunk c of key j is stored at chunk c ^ (j mod CH)
+//        -> the 16-byte Q·Kᵀ operand reads of 16 consecutive keys hit 16
+//           different chunks.
+//   V: chunk c of key j is stored at chunk c ^ (VSW·(j mod 4))
+//        -> the transposing 8-byte reads that build the P·V operand (4
+//           consecutive keys × 4 quads of d per 16-lane group) are spread
+//           over distinct banks.
 template <int D, int NW>
 struct Cfg {
   static constexpr int NT = NW * 64;          // threads per workgroup
   static constexpr int BM = NW * 32;          // query rows per workgroup
-  static constexpr int KP = D + 8;            // K tile row pitch (elements)
-  static constexpr int VP = kBN + 4;          // Vᵀ tile row pitch (elements)
-  static constexpr int K_ELEMS = kBN * KP;
-  static constexpr int V_ELEMS = D * VP;
-  static constexpr int CH = D / 8;            // 16-byte chunks per token row
-  static constexpr int UNITS = (kBN / 4) * CH; // staging units: 4 keys × 1 chunk
-  static constexpr int UPT = (UNITS + NT - 1) / NT;
-  static constexpr int LDS_BYTES = 2 * (K_ELEMS + V_ELEMS) * 2;
+  static constexpr int BN = LVSA_BN;          // keys per LDS tile
+  static constexpr int KB = BN / 32;          // 32-key MFMA blocks per tile
+  static constexpr int CH = D / 8;            // 16-byte chunks per key row
+  static constexpr int ROWB = D * 2;          // bytes per key row
+  static constexpr int TILE_BYTES = BN * ROWB;
+  static constexpr int LOADS = TILE_BYTES / 1024;      // 1 KB wave loads per tile
+  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  static constexpr int VSW = CH / 4;          // V swizzle step
+  static constexpr int KEYS_PER_LOAD = 64 / CH;       // keys per 1 KB wave load
+  static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES; // {K, V} × double buffer
+  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+};
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+
+// Word 3 of a raw buffer descriptor (CDNA: 32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
+// One workgroup's state and steps.  Kept in a struct so that the per-tile
+// step can be specialised on the LDS buffer (immediate LDS offsets) and on
+// whether the tile is the masked tail of a run.
+template <int D, int NW>
+struct Block {
+  using C = Cfg<D, NW>;
+
+  char *lds;
+  int lane, wave, l32, hf;
+  float scale_log2;
+  bf16x8_t qf[D / 16];        // Q rows of this wave, B-operand layout
+  f32x16_t oacc[D / 32];      // Oᵀ accumulators (dims × 32 queries)
+  float m_run;                // running row max, log2 domain (lazily raised)
+  float l_run;                // this lane's partial row sum
+  int32_t kro[D / 16];        // LDS byte offsets of this lane's K operands
+  int32_t vro[D / 32];        // LDS byte offsets of this lane's V source rows
+  int32_t koffb[C::LOADS_PER_WAVE], voffb[C::LOADS_PER_WAVE];  // load byte offsets
+
+  static constexpr int kTileOffK(int buf) { return buf * 2 * C::TILE_BYTES; }
+  static constexpr int kTileOffV(int buf) { return buf * 2 * C::TILE_BYTES + C::TILE_BYTES; }
+
+  __device__ __forceinline__ void init_offsets(int32_t k_sn, int32_t v_sn) {
+    // Load i of this wave covers keys key0 + i·KEYS_PER_LOAD (one per group
+    // of CH lanes); each lane writes stored chunk `pchunk` of its key's row,
+    // which holds logical chunk pchunk ^ swizzle(key).
+    const int key0 = wave * C::LOADS_PER_WAVE * C::KEYS_PER_LOAD + lane / C::CH;
+    const int pchunk = lane % C::CH;
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int key = key0 + i * C::KEYS_PER_LOAD;
+      koffb[i] = (key * (int32_t)k_sn + (pchunk ^ (key & (C::CH - 1))) * 8) * 2;
+      voffb[i] = (key * (int32_t)v_sn + (pchunk ^ (C::VSW * (key & 3))) * 8) * 2;
+    }
+    // K operand (Q·Kᵀ, A side): key kb·32 + l32, logical chunk 2·dc + hf.
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+      kro[dc] = l32 * C::ROWB + (((dc * 2 + hf) ^ (l32 & (C::CH - 1))) * 16);
+    // V operand (P·V, A side) by transposing 8-byte reads: in 16-lane group
+    // g, source lane s points at key 4·hf + s/4 (+ 16m + 8e per MFMA) and at
+    // dims 32·dc + 16·(g mod 2) + 4·(s mod 4) .. +3; the transpose then hands
+    // each lane its own dim for 4 consecutive keys.
+    const int s16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int dc = 0; dc < D / 32; ++dc) {
+      const int c = dc * 4 + (g & 1) * 2 + ((s16 & 3) >> 1);
+      vro[dc] = (4 * hf + (s16 >> 2)) * C::ROWB + ((c ^ (C::VSW * (s16 >> 2))) * 16) + (s16 & 1) * 8;
+    }
+  }
+
+  // Starts the direct global->LDS load of the K (or V) rows [pos, pos+kv)
+  // into LDS buffer `buf`.  The buffer descriptor ends at row pos+kv, so the
+  // rows of a run's tail tile past its end are filled with zeros by the
+  // hardware and nothing outside the run is read.
+  template <bool IS_V>
+  __device__ __forceinline__ void issue(int buf, const u16 *base, int32_t sn, int pos, int kv) {
+    const u16 *tb = base + (int64_t)pos * sn;
+    const int nrec = ((kv - 1) * (int32_t)sn + D) * 2;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, nrec, kBufferFlags);
+    char *dst = lds + (IS_V ? kTileOffV(buf) : kTileOffK(buf)) + wave * C::LOADS_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
+  }
+
+  // Sᵀ (keys × this wave's 32 queries) of the K tile in buffer KBUF.
+  template <int KBUF>
+  __device__ __forceinline__ void qk(f32x16_t (&sc)[C::KB]) const {
+    const char *Kb = lds + kTileOffK(KBUF);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) sc[kb] = f32x16_t{};
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kb * 32 * C::ROWB);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], sc[kb], 0, 0, 0);
+      }
+  }
+
+  // Probabilities of a tile whose maximum has been folded into m_run:
+  // P = 2^(S·scale·log2e − m_run) rounded to bf16, in the MFMA B-operand
+  // order of the P·V product; the row sum takes the same rounded values.
+  __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB]) {
+    const float neg_m = -m_run;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[kb * 2 + m][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][m * 8 + e], scale_log2, neg_m));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2_t pr = {pb[kb * 2 + m][e], pb[kb * 2 + m][e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        }
+      }
+  }
+
+  // One key tile from LDS buffer BUF: Sᵀ, mask and running max, P, P·V.
+  template <int BUF>
+  __device__ __forceinline__ void tile(int kv) {
+    f32x16_t sc[C::KB];
+    bf16x8_t pb[2 * C::KB];
+    qk<BUF>(sc);
+    fold_max(sc, kv);
+    probs(sc, pb);
+    pv<BUF>(pb);
+  }
+
+  // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF.
+  template <int VBUF>
+  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[2 * C::KB]) {
+    const char *Vb = lds + kTileOffV(VBUF);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int krow = (kb * 32 + m * 16) * C::ROWB;
+#pragma unroll
+        for (int dc = 0; dc < D / 32; ++dc) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow + 8 * C::ROWB));
+          const i16x8_t vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[kb * 2 + m],
+                                                             oacc[dc], 0, 0, 0);
+        }
+      }
+  }
+
+  // Masks the keys >= kv of a run's tail tile, folds the tile's row maximum
+  // into m_run (raised lazily, only when it would exceed it by more than
+  // 2^kMaxLag) and rescales O and the row sum when it moves.
+  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv) {
+    if (kv < C::BN) {
+      // Empty asm: keeps this wave-uniform branch a branch (no speculation
+      // of the selects into every tile).
+      asm volatile("" ::: "memory");
+      // element e of block kb is key kb·32 + 8·(e/4) + 4·hf + e%4; compare
+      // its lane-independent part against a per-lane threshold.
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const int thr = kv - kb * 32 - 4 * hf;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((e >> 2) * 8 + (e & 3) >= thr) sc[kb][e] = -INFINITY;
+      }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    mx = swap_halves_max(mx);
+    const float mt = mx * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kMaxLag) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+      m_run = m_new;
+    }
+  }
 };
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void lvsa_attn_fwd(Args a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
+void lvsa_attn_fwd(Args a) {
   using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * (C::K_ELEMS + C::V_ELEMS)];
-  u16 *const Ks0 = lds;
-  u16 *const Vt0 = lds + 2 * C::K_ELEMS;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];  // K0 V0 K1 V1
 
+  Block<D, NW> blk;
+  blk.lds = lds;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;  // which half of the wave
+  blk.lane = tid & 63;
+  blk.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  blk.l32 = blk.lane & 31;
+  blk.hf = blk.lane >> 5;
+  blk.scale_log2 = a.scale_log2;
 
   // ---- work item (XCD-contiguous remap of the dispatch order)
   int item;
@@ -154,20 +355,24 @@ __global__ __launch_bounds__(NW * 64) void lvsa_attn_fwd(Args a) {
   const u16 *vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
 
   // ---- Q fragment: 32 rows × D per wave, B-operand layout
-  const int q_row = qt * C::BM + wave * 32 + l32;  // row within frame t
+  const int q_row = qt * C::BM + blk.wave * 32 + blk.l32;  // row within frame t
   const bool q_ok = q_row < P;
-  const bool wave_live = (qt * C::BM + wave * 32) < P;  // wave-uniform
-  bf16x8_t qf[D / 16];
+  const bool wave_live = (qt * C::BM + blk.wave * 32) < P;  // wave-uniform
   {
     const u16 *qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
-                    ((int64_t)t * P + (q_ok ? q_row : 0)) * a.q_sn + hf * 8;
+                    ((int64_t)t * P + (q_ok ? q_row : 0)) * a.q_sn + blk.hf * 8;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
       bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(qp + dc * 16);
       if (!q_ok) x = bf16x8_t{};
-      qf[dc] = x;
+      blk.qf[dc] = x;
     }
   }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) blk.oacc[i] = f32x16_t{};
+  blk.m_run = -INFINITY;
+  blk.l_run = 0.f;
+  blk.init_offsets(a.k_sn, a.v_sn);
 
   // ---- CSR row -> runs of key frames
   RunIter it;
@@ -183,170 +388,57 @@ __global__ __launch_bounds__(NW * 64) void lvsa_attn_fwd(Args a) {
     it.ks = it.ke = 0;
   }
 
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16_t{};
-  float m_run = -INFINITY;  // running row max, log2 domain (lazy)
-  float l_run = 0.f;        // this lane's partial row sum
-
-  uint4 kreg[C::UPT][4], vreg[C::UPT][4];
-
-  auto load_tile = [&](int pos, int kv) {
-#pragma unroll
-    for (int u = 0; u < C::UPT; ++u) {
-      const int unit = tid + u * C::NT;
-      const int kg = unit % (kBN / 4), c = unit / (kBN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = kg * 4 + r;
-        uint4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-        if (unit < C::UNITS && j < kv) {
-          const int64_t tok = (int64_t)(pos + j);
-          kx = *reinterpret_cast<const uint4 *>(kbase + tok * a.k_sn + c * 8);
-          vx = *reinterpret_cast<const uint4 *>(vbase + tok * a.v_sn + c * 8);
-        }
-        kreg[u][r] = kx;
-        vreg[u][r] = vx;
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    u16 *Ks = Ks0 + buf * C::K_ELEMS;
-    u16 *Vt = Vt0 + buf * C::V_ELEMS;
-#pragma unroll
-    for (int u = 0; u < C::UPT; ++u) {
-      const int unit = tid + u * C::NT;
-      if (unit >= C::UNITS) continue;
-      const int kg = unit % (kBN / 4), c = unit / (kBN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<uint4 *>(Ks + (kg * 4 + r) * C::KP + c * 8) = kreg[u][r];
-      // transpose 4 keys × 8 dims into 8 rows of Vᵀ, 4 keys (8 bytes) each
-      const uint32_t w[4][4] = {
-          {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w},
-          {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w},
-          {vreg[u][2].x, vreg[u][2].y, vreg[u][2].z, vreg[u][2].w},
-          {vreg[u][3].x, vreg[u][3].y, vreg[u][3].z, vreg[u][3].w}};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wi = e >> 1;
-        uint2 pk;
-        if (e & 1) {
-          pk.x = pack_hi(w[0][wi], w[1][wi]);
-          pk.y = pack_hi(w[2][wi], w[3][wi]);
-        } else {
-          pk.x = pack_lo(w[0][wi], w[1][wi]);
-          pk.y = pack_lo(w[2][wi], w[3][wi]);
-        }
-        *reinterpret_cast<uint2 *>(Vt + (c * 8 + e) * C::VP + kg * 4) = pk;
-      }
-    }
-  };
-
-  auto compute_tile = [&](int buf, int kv) {
-    const u16 *Ks = Ks0 + buf * C::K_ELEMS;
-    const u16 *Vt = Vt0 + buf * C::V_ELEMS;
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const u16 *kp = Ks + (kb * 32 + l32) * C::KP + hf * 8;
-#pragma unroll
-      for (int dc = 0; dc < D / 16; ++dc) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(kp + dc * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], s[kb], 0, 0, 0);
-      }
-    }
-    if (kv < kBN) {  // tail tile of a run: keys >= kv are not in A(t)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-          if (key >= kv) s[kb][e] = -INFINITY;
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-    mx = swap_halves_max(mx);
-    const float mt = mx * a.scale_log2;
-    const bool need = mt > m_run + kMaxLag;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.scale_log2, neg_m));
-        s[kb][e] = p;
-        l_run += p;
-      }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][m * 8 + e];
-        const int key0 = kb * 32 + m * 16 + hf * 4;
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc) {
-          const u16 *vp = Vt + (dc * 32 + l32) * C::VP + key0;
-          const bf16x4_t lo = *reinterpret_cast<const bf16x4_t *>(vp);
-          const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(vp + 8);
-          const bf16x8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oacc[dc], 0, 0, 0);
-        }
-      }
-  };
-
-  // ---- main loop over key tiles (double-buffered LDS, one barrier per tile)
-  bool have = it.next_run();
-  int pos = it.ks;
-  int kv = have ? min(kBN, it.ke - pos) : 0;
-  if (have) {
-    load_tile(pos, kv);
-    store_tile(0);
+  // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
+  // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
+  // barrier per tile.  Unrolled by two so that every LDS offset is an
+  // immediate.
+  int n_tiles = 0;
+  {
+    RunIter c = it;
+    while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
   }
+  int pos = 0, kv = 0;
+  auto advance = [&]() {  // next tile, moving to the next run when needed
+    pos += C::BN;
+    if (pos >= it.ke) {
+      it.next_run();
+      pos = it.ks;
+    }
+    kv = min(C::BN, it.ke - pos);
+  };
+  auto issue = [&](int buf) {
+    blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
+    blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
+  };
+  if (n_tiles > 0) {
+    it.next_run();
+    pos = it.ks;
+    kv = min(C::BN, it.ke - pos);
+    issue(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int buf = 0;
-  while (have) {
-    // advance a copy of the iterator to the next tile
-    int npos = pos + kBN, nkv = 0;
-    bool has_next = true;
-    if (npos >= it.ke) {
-      has_next = it.next_run();
-      npos = it.ks;
-    }
-    if (has_next) {
-      nkv = min(kBN, it.ke - npos);
-      load_tile(npos, nkv);
-    }
-    if (wave_live) compute_tile(buf, kv);
-    if (has_next) store_tile(buf ^ 1);
+  for (int i = 0; i + 1 < n_tiles; i += 2) {
+    const int kv0 = kv;
+    advance();  // tile i+1 -> buffer 1
+    issue(1);
+    if (wave_live) blk.template tile<0>(kv0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (!has_next) break;
-    buf ^= 1;
-    pos = npos;
-    kv = nkv;
+    const int kv1 = kv;
+    if (i + 2 < n_tiles) {  // tile i+2 -> buffer 0
+      advance();
+      issue(0);
+    }
+    if (wave_live) blk.template tile<1>(kv1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
+  if ((n_tiles & 1) && wave_live) blk.template tile<0>(kv);
 
   // ---- epilogue: normalise, round to bf16, store
   if (!q_ok) return;
-  const float l_tot = swap_halves_sum(l_run);
+  const float l_tot = swap_halves_sum(blk.l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + q_row) * a.o_sn;
 #pragma unroll
@@ -355,8 +447,8 @@ __global__ __launch_bounds__(NW * 64) void lvsa_attn_fwd(Args a) {
     for (int i = 0; i < 4; ++i) {
       bf16x4_t r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = (__bf16)(oacc[dc][i * 4 + j] * inv);
-      *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + hf * 4) = r;
+      for (int j = 0; j < 4; ++j) r[j] = (__bf16)(blk.oacc[dc][i * 4 + j] * inv);
+      *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + blk.hf * 4) = r;
     }
 }
 
@@ -391,6 +483,8 @@ int check_tensor(const lvsa_tensor *x, const char *name) {
   if (reinterpret_cast<uintptr_t>(x->data) % 16) return lvsa::fail(LVSA_ERR_SHAPE, "%s: data not 16-byte aligned", name);
   if (x->stride_n < x->D || x->stride_b < 0 || x->stride_h < 0 || x->stride_n % 8 || x->stride_h % 8 || x->stride_b % 8)
     return lvsa::fail(LVSA_ERR_SHAPE, "%s: strides must be multiples of 8 elements with stride_n >= D", name);
+  if (x->stride_n > (int64_t{1} << 24))
+    return lvsa::fail(LVSA_ERR_SHAPE, "%s: stride_n above 2^24 elements is not supported", name);
   return LVSA_OK;
 }
 
@@ -442,7 +536,7 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
 
   const int D = (int)q->D;
   const int P = (int)(q->N / T);
-  constexpr int NW = 4;
+  constexpr int NW = LVSA_NW;
   const int BM = NW * 32;
   const int q_tiles = (P + BM - 1) / BM;
   const int64_t n_wg = (int64_t)q->B * q->H * T * q_tiles;
@@ -453,10 +547,10 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   a.k = static_cast<const u16 *>(k->data);
   a.v = static_cast<const u16 *>(v->data);
   a.o = static_cast<u16 *>(out->data);
-  a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sn = q->stride_n;
-  a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sn = k->stride_n;
-  a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sn = v->stride_n;
-  a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sn = out->stride_n;
+  a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sn = (int32_t)q->stride_n;
+  a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sn = (int32_t)k->stride_n;
+  a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sn = (int32_t)v->stride_n;
+  a.o_sb = out->stride_b; a.o_sh = out->stride_h; a.o_sn = (int32_t)out->stride_n;
   a.row_ptr = row_ptr_dev;
   a.col_idx = col_idx_dev;
   a.nnz = nnz;
