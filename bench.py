@@ -219,7 +219,7 @@ def main():
     traffic = measured_traffic(w, 1)
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "kernel": "lvsa_attn_fwd<128,4>", "kernel_ms_avg": round(k_avg, 4)}
+            "kernel": "lvsa_attn_fwd<128,4,1>", "kernel_ms_avg": round(k_avg, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -45,6 +45,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 #include "lvsa_internal.h"
 
@@ -63,10 +64,16 @@ typedef uint16_t u16;
 #define LVSA_NW 4
 #endif
 #ifndef LVSA_WAVES_PER_SIMD
-#define LVSA_WAVES_PER_SIMD 2
+#define LVSA_WAVES_PER_SIMD 3
 #endif
 #ifndef LVSA_BN
-#define LVSA_BN 64
+#define LVSA_BN 32
+#endif
+#ifndef LVSA_QB
+#define LVSA_QB 1
+#endif
+#ifndef LVSA_STAGES
+#define LVSA_STAGES 2
 #endif
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
@@ -126,10 +133,11 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 //        -> the transposing 8-byte reads that build the P·V operand (4
 //           consecutive keys × 4 quads of d per 16-lane group) are spread
 //           over distinct banks.
-template <int D, int NW>
+template <int D, int NW, int QB>
 struct Cfg {
   static constexpr int NT = NW * 64;          // threads per workgroup
-  static constexpr int BM = NW * 32;          // query rows per workgroup
+  static constexpr int QROWS = 32 * QB;       // query rows per wave (QB blocks of 32)
+  static constexpr int BM = NW * QROWS;       // query rows per workgroup
   static constexpr int BN = LVSA_BN;          // keys per LDS tile
   static constexpr int KB = BN / 32;          // 32-key MFMA blocks per tile
   static constexpr int CH = D / 8;            // 16-byte chunks per key row
@@ -139,7 +147,8 @@ struct Cfg {
   static constexpr int LOADS_PER_WAVE = LOADS / NW;
   static constexpr int VSW = CH / 4;          // V swizzle step
   static constexpr int KEYS_PER_LOAD = 64 / CH;       // keys per 1 KB wave load
-  static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES; // {K, V} × double buffer
+  static constexpr int STAGES = LVSA_STAGES;          // LDS tile buffers (loads run STAGES-1 tiles ahead)
+  static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES; // {K, V} × STAGES
   static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
 };
 
@@ -151,22 +160,24 @@ typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 // Word 3 of a raw buffer descriptor (CDNA: 32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
-// One workgroup's state and steps.  Kept in a struct so that the per-tile
-// step can be specialised on the LDS buffer (immediate LDS offsets) and on
-// whether the tile is the masked tail of a run.
-template <int D, int NW>
+// One wave's state and steps.  Kept in a struct so that the per-tile step
+// can be specialised on the LDS buffer (immediate LDS offsets).  A wave owns
+// QB blocks of 32 query rows; every K and V operand read from LDS feeds QB
+// MFMAs.
+template <int D, int NW, int QB>
 struct Block {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, QB>;
 
   char *lds;
   int lane, wave, l32, hf;
   float scale_log2;
-  bf16x8_t qf[D / 16];        // Q rows of this wave, B-operand layout
-  f32x16_t oacc[D / 32];      // Oᵀ accumulators (dims × 32 queries)
-  float m_run;                // running row max, log2 domain (lazily raised)
-  float l_run;                // this lane's partial row sum
-  int32_t kro[D / 16];        // LDS byte offsets of this lane's K operands
-  int32_t vro[D / 32];        // LDS byte offsets of this lane's V source rows
+  bool live[QB];               // block has at least one row inside the frame (wave-uniform)
+  bf16x8_t qf[QB][D / 16];     // Q rows, B-operand layout
+  f32x16_t oacc[QB][D / 32];   // Oᵀ accumulators (dims × 32 queries)
+  float m_run[QB];             // running row max, log2 domain (lazily raised)
+  float l_run[QB];             // this lane's partial row sum
+  int32_t kro[D / 16];         // LDS byte offsets of this lane's K operands
+  int32_t vro[D / 32];         // LDS byte offsets of this lane's V source rows
   int32_t koffb[C::LOADS_PER_WAVE], voffb[C::LOADS_PER_WAVE];  // load byte offsets
 
   static constexpr int kTileOffK(int buf) { return buf * 2 * C::TILE_BYTES; }
@@ -181,8 +192,8 @@ struct Block {
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
       const int key = key0 + i * C::KEYS_PER_LOAD;
-      koffb[i] = (key * (int32_t)k_sn + (pchunk ^ (key & (C::CH - 1))) * 8) * 2;
-      voffb[i] = (key * (int32_t)v_sn + (pchunk ^ (C::VSW * (key & 3))) * 8) * 2;
+      koffb[i] = (key * k_sn + (pchunk ^ (key & (C::CH - 1))) * 8) * 2;
+      voffb[i] = (key * v_sn + (pchunk ^ (C::VSW * (key & 3))) * 8) * 2;
     }
     // K operand (Q·Kᵀ, A side): key kb·32 + l32, logical chunk 2·dc + hf.
 #pragma unroll
@@ -207,7 +218,7 @@ struct Block {
   template <bool IS_V>
   __device__ __forceinline__ void issue(int buf, const u16 *base, int32_t sn, int pos, int kv) {
     const u16 *tb = base + (int64_t)pos * sn;
-    const int nrec = ((kv - 1) * (int32_t)sn + D) * 2;
+    const int nrec = ((kv - 1) * sn + D) * 2;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, nrec, kBufferFlags);
     char *dst = lds + (IS_V ? kTileOffV(buf) : kTileOffK(buf)) + wave * C::LOADS_PER_WAVE * 1024;
 #pragma unroll
@@ -215,77 +226,29 @@ struct Block {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
   }
 
-  // Sᵀ (keys × this wave's 32 queries) of the K tile in buffer KBUF.
+  // Sᵀ (keys × 32 queries per block) of the K tile in buffer KBUF.
   template <int KBUF>
-  __device__ __forceinline__ void qk(f32x16_t (&sc)[C::KB]) const {
+  __device__ __forceinline__ void qk(f32x16_t (&sc)[QB][C::KB]) const {
     const char *Kb = lds + kTileOffK(KBUF);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) sc[kb] = f32x16_t{};
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) sc[q][kb] = f32x16_t{};
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kb * 32 * C::ROWB);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], sc[kb], 0, 0, 0);
-      }
-  }
-
-  // Probabilities of a tile whose maximum has been folded into m_run:
-  // P = 2^(S·scale·log2e − m_run) rounded to bf16, in the MFMA B-operand
-  // order of the P·V product; the row sum takes the same rounded values.
-  __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB]) {
-    const float neg_m = -m_run;
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[kb * 2 + m][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][m * 8 + e], scale_log2, neg_m));
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2_t pr = {pb[kb * 2 + m][e], pb[kb * 2 + m][e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
-        }
-      }
-  }
-
-  // One key tile from LDS buffer BUF: Sᵀ, mask and running max, P, P·V.
-  template <int BUF>
-  __device__ __forceinline__ void tile(int kv) {
-    f32x16_t sc[C::KB];
-    bf16x8_t pb[2 * C::KB];
-    qk<BUF>(sc);
-    fold_max(sc, kv);
-    probs(sc, pb);
-    pv<BUF>(pb);
-  }
-
-  // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF.
-  template <int VBUF>
-  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[2 * C::KB]) {
-    const char *Vb = lds + kTileOffV(VBUF);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int krow = (kb * 32 + m * 16) * C::ROWB;
-#pragma unroll
-        for (int dc = 0; dc < D / 32; ++dc) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow + 8 * C::ROWB));
-          const i16x8_t vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[kb * 2 + m],
-                                                             oacc[dc], 0, 0, 0);
-        }
+        for (int q = 0; q < QB; ++q)
+          if (live[q]) sc[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[q][dc], sc[q][kb], 0, 0, 0);
       }
   }
 
   // Masks the keys >= kv of a run's tail tile, folds the tile's row maximum
   // into m_run (raised lazily, only when it would exceed it by more than
   // 2^kMaxLag) and rescales O and the row sum when it moves.
-  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv) {
+  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv, int q) {
     if (kv < C::BN) {
       // Empty asm: keeps this wave-uniform branch a branch (no speculation
       // of the selects into every tile).
@@ -307,26 +270,87 @@ struct Block {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
     mx = swap_halves_max(mx);
     const float mt = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kMaxLag) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run[q] + kMaxLag) != 0) {
+      const float m_new = fmaxf(m_run[q], mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
+      l_run[q] *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-      m_run = m_new;
+        for (int e = 0; e < 16; ++e) oacc[q][i][e] *= alpha;
+      m_run[q] = m_new;
+    }
+  }
+
+  // Probabilities of a tile whose maximum has been folded into m_run:
+  // P = 2^(S·scale·log2e − m_run) rounded to bf16, in the MFMA B-operand
+  // order of the P·V product; the row sum takes the same rounded values, so
+  // the normalised weights sum to one.
+  __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB], int q) {
+    const float neg_m = -m_run[q];
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[kb * 2 + m][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][m * 8 + e], scale_log2, neg_m));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2_t pr = {pb[kb * 2 + m][e], pb[kb * 2 + m][e + 1]};
+          l_run[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[q], false);
+        }
+      }
+  }
+
+  // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF, for the query blocks in
+  // [q0, q1).
+  template <int VBUF>
+  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[QB][2 * C::KB], int q0, int q1) {
+    const char *Vb = lds + kTileOffV(VBUF);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int krow = (kb * 32 + m * 16) * C::ROWB;
+#pragma unroll
+        for (int dc = 0; dc < D / 32; ++dc) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow + 8 * C::ROWB));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            if (q >= q0 && q < q1 && live[q])
+              oacc[q][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[q][kb * 2 + m], oacc[q][dc], 0, 0, 0);
+        }
+      }
+  }
+
+  // One key tile from LDS buffer BUF.  With two query blocks the softmax of
+  // the second block runs while the P·V MFMAs of the first are in flight.
+  template <int BUF>
+  __device__ __forceinline__ void tile(int kv) {
+    f32x16_t sc[QB][C::KB];
+    bf16x8_t pb[QB][2 * C::KB];
+    qk<BUF>(sc);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (!live[q]) continue;
+      fold_max(sc[q], kv, q);
+      probs(sc[q], pb[q], q);
+      pv<BUF>(pb, q, q + 1);
     }
   }
 };
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
 void lvsa_attn_fwd(Args a) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, QB>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];  // K0 V0 K1 V1
 
-  Block<D, NW> blk;
+  Block<D, NW, QB> blk;
   blk.lds = lds;
   const int tid = threadIdx.x;
   blk.lane = tid & 63;
@@ -354,24 +378,28 @@ void lvsa_attn_fwd(Args a) {
   const u16 *kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const u16 *vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
 
-  // ---- Q fragment: 32 rows × D per wave, B-operand layout
-  const int q_row = qt * C::BM + blk.wave * 32 + blk.l32;  // row within frame t
-  const bool q_ok = q_row < P;
-  const bool wave_live = (qt * C::BM + blk.wave * 32) < P;  // wave-uniform
-  {
-    const u16 *qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh +
-                    ((int64_t)t * P + (q_ok ? q_row : 0)) * a.q_sn + blk.hf * 8;
+  // ---- Q fragments: QB blocks of 32 rows × D per wave, B-operand layout
+  const int row0 = qt * C::BM + blk.wave * C::QROWS;  // first row of this wave within frame t
+  bool any_live = false;
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    blk.live[q] = row0 + q * 32 < P;  // wave-uniform
+    any_live |= blk.live[q];
+    const int r = row0 + q * 32 + blk.l32;
+    const bool ok = r < P;
+    const u16 *qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + ((int64_t)t * P + (ok ? r : 0)) * a.q_sn +
+                    blk.hf * 8;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
       bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(qp + dc * 16);
-      if (!q_ok) x = bf16x8_t{};
-      blk.qf[dc] = x;
+      if (!ok) x = bf16x8_t{};
+      blk.qf[q][dc] = x;
     }
-  }
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) blk.oacc[i] = f32x16_t{};
-  blk.m_run = -INFINITY;
-  blk.l_run = 0.f;
+    for (int i = 0; i < D / 32; ++i) blk.oacc[q][i] = f32x16_t{};
+    blk.m_run[q] = -INFINITY;
+    blk.l_run[q] = 0.f;
+  }
   blk.init_offsets(a.k_sn, a.v_sn);
 
   // ---- CSR row -> runs of key frames
@@ -388,6 +416,69 @@ void lvsa_attn_fwd(Args a) {
     it.ks = it.ke = 0;
   }
 
+#if LVSA_STAGES == 3
+  // ---- main loop over key tiles: K and V triple-buffered in LDS (tile j in
+  // buffer j mod 3); the loads of tile j+2 are issued before tile j is
+  // computed, and each tile's end waits only for tile j+1's loads; one
+  // barrier per tile.  Unrolled by three so that every LDS offset is an
+  // immediate.
+  int n_tiles = 0;
+  {
+    RunIter c = it;
+    while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
+  }
+  int pos = 0, kv = 0;
+  auto advance = [&]() {  // next tile, moving to the next run when needed
+    pos += C::BN;
+    if (pos >= it.ke) {
+      it.next_run();
+      pos = it.ks;
+    }
+    kv = min(C::BN, it.ke - pos);
+  };
+  auto issue = [&](int buf) {
+    blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
+    blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
+  };
+  int kvq0 = 0, kvq1 = 0;  // valid keys of the next two tiles to compute
+  if (n_tiles > 0) {
+    it.next_run();
+    pos = it.ks;
+    kv = min(C::BN, it.ke - pos);
+    issue(0);
+    kvq0 = kv;
+  }
+  if (n_tiles > 1) {
+    advance();
+    issue(1);
+    kvq1 = kv;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS_PER_WAVE) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  // step: compute tile j (buffer B) while tile j+2 loads into buffer (B+2)%3
+  auto step = [&](auto bufc, int j) {
+    constexpr int B = decltype(bufc)::value;
+    const int kvj = kvq0;
+    kvq0 = kvq1;
+    const bool more = j + 2 < n_tiles;
+    if (more) {
+      advance();
+      issue((B + 2) % 3);
+      kvq1 = kv;
+    }
+    if (any_live) blk.template tile<B>(kvj);
+    if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS_PER_WAVE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 3) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
+    if (j + 2 < n_tiles) step(std::integral_constant<int, 2>{}, j + 2);
+  }
+#else
   // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
   // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
   // barrier per tile.  Unrolled by two so that every LDS offset is an
@@ -422,7 +513,7 @@ void lvsa_attn_fwd(Args a) {
     const int kv0 = kv;
     advance();  // tile i+1 -> buffer 1
     issue(1);
-    if (wave_live) blk.template tile<0>(kv0);
+    if (any_live) blk.template tile<0>(kv0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int kv1 = kv;
@@ -430,26 +521,33 @@ void lvsa_attn_fwd(Args a) {
       advance();
       issue(0);
     }
-    if (wave_live) blk.template tile<1>(kv1);
+    if (any_live) blk.template tile<1>(kv1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if ((n_tiles & 1) && wave_live) blk.template tile<0>(kv);
+  if ((n_tiles & 1) && any_live) blk.template tile<0>(kv);
+
+#endif
 
   // ---- epilogue: normalise, round to bf16, store
-  if (!q_ok) return;
-  const float l_tot = swap_halves_sum(blk.l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + q_row) * a.o_sn;
 #pragma unroll
-  for (int dc = 0; dc < D / 32; ++dc)
+  for (int q = 0; q < QB; ++q) {
+    const int r = row0 + q * 32 + blk.l32;
+    // both lane halves hold the same row: reduce before the early exit
+    const float l_tot = swap_halves_sum(blk.l_run[q]);
+    if (r >= P) continue;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + r) * a.o_sn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x4_t r;
+    for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = (__bf16)(blk.oacc[dc][i * 4 + j] * inv);
-      *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + blk.hf * 4) = r;
-    }
+      for (int i = 0; i < 4; ++i) {
+        bf16x4_t o4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(blk.oacc[q][dc][i * 4 + j] * inv);
+        *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + blk.hf * 4) = o4;
+      }
+  }
 }
 
 // ------------------------------------------------------------------ host --
@@ -502,9 +600,9 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
   return a0 < b1 && b0 < a1;
 }
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 int launch(const Args &args, hipStream_t stream) {
-  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW, QB>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return lvsa::ok();
@@ -537,7 +635,8 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   const int D = (int)q->D;
   const int P = (int)(q->N / T);
   constexpr int NW = LVSA_NW;
-  const int BM = NW * 32;
+  constexpr int QB = LVSA_QB;
+  const int BM = NW * 32 * QB;
   const int q_tiles = (P + BM - 1) / BM;
   const int64_t n_wg = (int64_t)q->B * q->H * T * q_tiles;
   if (n_wg > INT32_MAX) return lvsa::fail(LVSA_ERR_SHAPE, "grid of %lld workgroups too large", (long long)n_wg);
@@ -563,6 +662,6 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   a.scale_log2 = sc * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128) return launch<128, NW>(a, s);
-  return launch<64, NW>(a, s);
+  if (D == 128) return launch<128, NW, QB>(a, s);
+  return launch<64, NW, QB>(a, s);
 }
