@@ -3,18 +3,24 @@
 One step = one denoising step of the attention hot path over the whole
 workload: build the step's CSR mask on the host (C++), copy it to the device,
 run the frame-block-sparse attention kernel on [B, H, T·P, d] bf16.  The
-workload is the Wan-2.1-1.3B-shaped 6× horizon: B=1, H=12, d=128, T=121
-latent frames × 1560 tokens (480×832 video), C=21, W=9, anchors rotating
-with the step (seeded synthetic N(0,1) inputs, resident in HBM before the
-timed region).
+default workload is the Wan-2.1-1.3B-shaped 6× horizon: B=1, H=12, d=128,
+T=121 latent frames × 1560 tokens (480×832 video), C=21, W=9, anchors
+rotating with the step (seeded synthetic N(0,1) inputs, resident in HBM before
+the timed region).
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
-  value      effective TFLOP/s = algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d per
-             step ÷ time per step (padding and softmax not counted)
-  roofline   for the attention kernel, from HIP events around each launch
+  value         effective TFLOP/s = algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d
+                per step ÷ time per step (padding and softmax not counted)
+  roofline      the attention kernel: HIP events around each launch on its
+                stream; HBM bytes from the committed rocprofv3 summary
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same step
+  also          per-call kernel median/p10/p90, host mask build and mask H2D
+                times, dense comparator (same kernel, C = T mask) and speedup,
+                peak device memory; for workloads at the training horizon
+                (T <= C) the full-step / dense-kernel time ratio.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan13b_6x]
+    python bench.py --sweep [--sweep-out FILE]   # every workload, table on stderr
 """
 
 from __future__ import annotations
@@ -24,6 +30,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +42,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "LVSA attention effective TFLOP/s + ms/call, T=121×1560 tok, H=12 d=128 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_wan13b_6x.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_lvsa_amd", "csrc", "attention.hip")]
+SWEEP = ["wan13b_1x", "syn_1p5x", "syn_2x", "wan13b_6x", "wan14b_6x"]
 
 
 def log(*a):
@@ -53,7 +61,7 @@ def algorithmic_flops(w) -> float:
     return 4.0 * w.B * w.H * w.T * min(w.C, w.T) * w.P * w.P * w.D
 
 
-def measured_traffic(w, n_launch_units: float):
+def measured_traffic(w):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
     when it is missing or was taken on a different kernel source."""
     try:
@@ -92,35 +100,24 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wan13b_6x")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              f"multi-GPU path.", file=sys.stderr)
-        sys.exit(2)
+def pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(p * len(xs)))]
 
+
+def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False):
+    """Times `steps` full hot-path steps of workload `w`; returns a dict."""
     import torch
     import block_sparse_attention_lvsa_amd as L
-    from block_sparse_attention_lvsa_amd.synth import WORKLOADS, make_qkv
+    from block_sparse_attention_lvsa_amd.synth import make_qkv
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     lib = L.library()
-    log(f"workload {w}")
+    torch.cuda.reset_peak_memory_stats(dev)
     q, k, v = make_qkv(w, device=dev)
     out = torch.empty_like(q)
     torch.cuda.synchronize()
-    if args.calib_copy:
+    if calib_copy:
         # Reads exactly 2^30 bytes and writes 2^30 bytes per launch: the
         # reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE readings.
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -132,7 +129,7 @@ def main():
 
     T, C, W = w.T, w.C, w.W
     nnz = L.lvsa_mask_nnz(T, C, W)
-    total = args.warmup + args.steps
+    total = warmup + steps
     # One pinned host buffer pair per step (the host never rewrites a buffer
     # whose copy may still be pending) and one device pair (same stream, so
     # copy s+1 runs after kernel s).
@@ -146,7 +143,7 @@ def main():
     sp = ctypes.c_void_p(stream.cuda_stream)
     I32P = ctypes.POINTER(ctypes.c_int32)
 
-    def step(i: int, s: int, ev=None, mask_times=None):
+    def step(i, s, ev=None, mask_times=None):
         t0 = time.perf_counter()
         rc = lib.lvsa_build_mask(T, C, W, s, L.LVSA_ROT_MOD_TPER,
                                  ctypes.cast(ctypes.c_void_p(h_rp[i].data_ptr()), I32P),
@@ -155,85 +152,160 @@ def main():
             mask_times.append(time.perf_counter() - t0)
         if rc:
             raise RuntimeError(L.lvsa_last_error())
+        if ev is not None:
+            ev[0].record(stream)
         d_rp.copy_(h_rp[i], non_blocking=True)
         d_ci.copy_(h_ci[i], non_blocking=True)
         if ev is not None:
-            ev[0].record(stream)
+            ev[1].record(stream)
         rc = lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
                                 ctypes.c_void_p(d_rp.data_ptr()), ctypes.c_void_p(d_ci.data_ptr()),
                                 T, nnz, ctypes.byref(recs[3]), 0.0, sp)
         if ev is not None:
-            ev[1].record(stream)
+            ev[2].record(stream)
         if rc:
             raise RuntimeError(L.lvsa_last_error())
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, i)
     torch.cuda.synchronize()
 
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     mask_times = []
     g0 = torch.cuda.Event(enable_timing=True)
     g1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     g0.record(stream)
-    for j in range(args.steps):
-        step(args.warmup + j, j, kev[j], mask_times)
+    for j in range(steps):
+        step(warmup + j, j, ev[j], mask_times)
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = g0.elapsed_time(g1)
-    ms_per_step = max(total_ms, wall * 1e3) / args.steps
-    kms = sorted(a.elapsed_time(b) for a, b in kev)
-    k_avg = sum(kms) / len(kms)
+    ms_per_step = max(g0.elapsed_time(g1), wall * 1e3) / steps
+    kms = [e[1].elapsed_time(e[2]) for e in ev]
+    h2d = [e[0].elapsed_time(e[1]) for e in ev]
     flops = algorithmic_flops(w)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (k_avg * 1e-3) / 1e12
-    log(f"step: {ms_per_step:.3f} ms  kernel avg {k_avg:.3f} ms (p10 {kms[len(kms) // 10]:.3f}, "
-        f"p90 {kms[(9 * len(kms)) // 10]:.3f})  {value:.1f} TFLOP/s effective, kernel {achieved:.1f} TFLOP/s")
-    log(f"host mask build: median {sorted(mask_times)[len(mask_times) // 2] * 1e6:.1f} us/step")
-
-    extra = {}
-    if not args.no_dense:
+    k_avg = sum(kms) / len(kms)
+    res = {
+        "workload": w.name,
+        "ms_per_step": ms_per_step,
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "kernel_ms": {"avg": k_avg, "median": statistics.median(kms), "p10": pct(kms, 0.1), "p90": pct(kms, 0.9)},
+        "kernel_tflops": flops / (k_avg * 1e-3) / 1e12,
+        "mask_build_us_median": statistics.median(mask_times) * 1e6,
+        "mask_h2d_ms_median": statistics.median(h2d),
+        "flops_per_step": flops,
+    }
+    if dense:
         # Dense comparator: the same kernel with a C = T mask (one run of N keys).
-        dm = L.lvsa_build_mask(T, max(T, 2), 1, 0)
-        if True:
-            dmd = dm.to(dev)
-            reps = 3
-            L.lvsa_attention(q, k, v, dmd, out=out)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                L.lvsa_attention(q, k, v, dmd, out=out)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            dense_ms = e0.elapsed_time(e1) / reps
-            extra = {"dense_ms_per_call": round(dense_ms, 3),
-                     "speedup_vs_dense_kernel": round(dense_ms / k_avg, 3),
-                     "ideal_speedup_T_over_C": round(T / min(C, T), 3)}
-            log(f"dense (C=T) kernel: {dense_ms:.3f} ms -> speedup {dense_ms / k_avg:.2f}x (ideal {T / min(C, T):.2f}x)")
+        dm = L.lvsa_build_mask(T, max(T, 2), 1, 0).to(dev)
+        L.lvsa_attention(q, k, v, dm, out=out)
+        torch.cuda.synchronize()
+        reps = 3
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            L.lvsa_attention(q, k, v, dm, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        res["dense_ms_per_call"] = dense_ms
+        res["speedup_vs_dense_kernel"] = dense_ms / k_avg
+        res["ideal_speedup_T_over_C"] = T / min(C, T)
+        if T <= C:
+            # At the training horizon the method is the dense model: the full
+            # step (host mask + H2D + kernel) against the dense kernel alone.
+            res["full_step_over_dense_kernel"] = ms_per_step / dense_ms
+    res["max_memory_allocated_gb"] = torch.cuda.max_memory_allocated(dev) / 1e9
+    if keep_inputs:
+        res["_inputs"] = (q, k, v)
+    return res
 
-    traffic = measured_traffic(w, 1)
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan13b_6x")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true", help="time every workload (table on stderr)")
+    ap.add_argument("--sweep-out", default=None, help="also write the sweep table (markdown) here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_lvsa_amd.synth import WORKLOADS
+
+    if args.sweep:
+        lines = ["| workload | B·H, T×P, C/W | ms/call (median) | effective TFLOP/s | % of 2.5 PF | dense (C=T) ms | "
+                 "speedup | ideal T/C | full step / dense (T≤C) | peak mem GB |",
+                 "|---|---|---|---|---|---|---|---|---|---|"]
+        for name in SWEEP:
+            w = WORKLOADS[name]
+            r = run_workload(w, args.steps, args.warmup, dense=True)
+            log(json.dumps(r))
+            ov = r.get("full_step_over_dense_kernel")
+            lines.append(f"| {name} | {w.B * w.H}, {w.T}×{w.P}, {w.C}/{w.W} | {r['kernel_ms']['median']:.3f} | "
+                         f"{r['kernel_tflops']:.1f} | {100 * r['kernel_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
+                         f"{r['dense_ms_per_call']:.3f} | {r['speedup_vs_dense_kernel']:.2f} | "
+                         f"{r['ideal_speedup_T_over_C']:.2f} | {'%.3f' % ov if ov else '—'} | "
+                         f"{r['max_memory_allocated_gb']:.1f} |")
+            torch.cuda.empty_cache()
+        table = "\n".join(lines)
+        log(table)
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                f.write(table + "\n")
+        return
+
+    w = WORKLOADS[args.workload]
+    log(f"workload {w}")
+    r = run_workload(w, args.steps, args.warmup, dense=not args.no_dense, calib_copy=args.calib_copy,
+                     keep_inputs=not args.no_cpu_baseline)
+    log(f"step: {r['ms_per_step']:.3f} ms  kernel avg {r['kernel_ms']['avg']:.3f} ms (median "
+        f"{r['kernel_ms']['median']:.3f}, p10 {r['kernel_ms']['p10']:.3f}, p90 {r['kernel_ms']['p90']:.3f})  "
+        f"{r['value']:.1f} TFLOP/s effective, kernel {r['kernel_tflops']:.1f} TFLOP/s")
+    log(f"host mask build: median {r['mask_build_us_median']:.1f} us/step; mask H2D median "
+        f"{r['mask_h2d_ms_median'] * 1e3:.1f} us/step")
+    if "dense_ms_per_call" in r:
+        log(f"dense (C=T) kernel: {r['dense_ms_per_call']:.3f} ms -> speedup {r['speedup_vs_dense_kernel']:.2f}x "
+            f"(ideal {r['ideal_speedup_T_over_C']:.2f}x)")
+
+    achieved = r["kernel_tflops"]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-            "kernel": "lvsa_attn_fwd<128,4,1>", "kernel_ms_avg": round(k_avg, 4)}
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
+            "kernel": "lvsa_attn_fwd<128,4,1>", "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
+        q, k, v = r.pop("_inputs")
         cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads ({cpu['sample']})")
 
+    extra = {key: (round(val, 4) if isinstance(val, float) else val) for key, val in r.items()
+             if key in ("dense_ms_per_call", "speedup_vs_dense_kernel", "ideal_speedup_T_over_C",
+                        "full_step_over_dense_kernel", "mask_build_us_median", "mask_h2d_ms_median",
+                        "max_memory_allocated_gb")}
+    extra["kernel_ms"] = {key: round(val, 4) for key, val in r["kernel_ms"].items()}
     rec = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(r["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -241,7 +313,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "P": w.P, "d": w.D, "C": w.C, "W": w.W,
                    "tokens": w.N, "rotation": "mod_tper", "denoising_steps": f"0..{args.steps - 1}",
-                   "flops_per_step": flops, "parallelism": "single-gpu"},
+                   "flops_per_step": r["flops_per_step"], "parallelism": "single-gpu"},
         "roofline": roof,
         "cpu_baseline": cpu,
         **extra,

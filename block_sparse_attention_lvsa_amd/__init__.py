@@ -38,6 +38,7 @@ LVSA_ERR_MASK = -6
 LVSA_ROT_MOD_TPER = 0
 LVSA_ROT_MOD_T = 1
 LVSA_FIXED_GRID = 2
+LVSA_WINDOW_ONLY = 3
 
 LVSA_DTYPE_BF16 = 1
 

@@ -26,7 +26,8 @@ int check_domain(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags) {
   if (C < 2) return lvsa::fail(LVSA_ERR_ARG, "C=%d: need C >= 2", C);
   if (W < 1 || W > C - 1) return lvsa::fail(LVSA_ERR_ARG, "W=%d: need 1 <= W <= C-1 (C=%d)", W, C);
   if (step < 0) return lvsa::fail(LVSA_ERR_ARG, "step=%d: need step >= 0", step);
-  if (flags != LVSA_ROT_MOD_TPER && flags != LVSA_ROT_MOD_T && flags != LVSA_FIXED_GRID)
+  if (flags != LVSA_ROT_MOD_TPER && flags != LVSA_ROT_MOD_T && flags != LVSA_FIXED_GRID &&
+      flags != LVSA_WINDOW_ONLY)
     return lvsa::fail(LVSA_ERR_ARG, "flags=%d: unknown rotation flag", flags);
   return LVSA_OK;
 }
@@ -67,9 +68,11 @@ extern "C" int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, in
     return lvsa::ok();
   }
 
-  // Anchor schedule: spacing, count, offset of this step.
-  const int32_t t_per = (T + (C - W) - 1) / (C - W);
-  const int32_t n_g = (T + t_per - 1) / t_per;
+  // Anchor schedule: spacing, count, offset of this step (no anchors for the
+  // window-only ablation).
+  const bool anchored = flags != LVSA_WINDOW_ONLY;
+  const int32_t t_per = anchored ? (T + (C - W) - 1) / (C - W) : 0;
+  const int32_t n_g = anchored ? (T + t_per - 1) / t_per : 0;
   int32_t o = 0;
   if (flags == LVSA_ROT_MOD_TPER) o = step % t_per;
   else if (flags == LVSA_ROT_MOD_T) o = step % T;

@@ -46,10 +46,15 @@ extern "C" {
  *     cyclically over the frame count (TechWalker article, §三).  Identical
  *     to the default whenever Tper divides T.
  *   LVSA_FIXED_GRID: o_s = 0 at every step, the non-rotating grid the pages
- *     describe as the cause of fixed-grid bias (ablation). */
+ *     describe as the cause of fixed-grid bias (ablation).
+ *   LVSA_WINDOW_ONLY: no anchors; A(t) = the min(C, T) frames nearest to t
+ *     (ties to the lower index), i.e. plain sliding-window attention, the
+ *     prior-art pattern the pages contrast LVSA with (ablation; t_per and
+ *     n_anchor are reported as 0). */
 #define LVSA_ROT_MOD_TPER 0
 #define LVSA_ROT_MOD_T    1
 #define LVSA_FIXED_GRID   2
+#define LVSA_WINDOW_ONLY  3
 
 /* Element types. */
 #define LVSA_DTYPE_BF16 1
@@ -99,7 +104,7 @@ int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out);
  * Definition (readings of the pages where they leave a step open):
  *   T <= C : every row is 0..T-1 (dense; at the training horizon the method
  *            is the dense model).
- *   T >  C : Tper = ceil(T/(C-W)), n_g = ceil(T/Tper),
+ *   T >  C, flags != LVSA_WINDOW_ONLY : Tper = ceil(T/(C-W)), n_g = ceil(T/Tper),
  *            G = { (o_s + k*Tper) mod T : 0 <= k < n_g }, o_s per flags;
  *            W(t) = the C - n_g non-anchor frames nearest to t, ties to the
  *            lower frame index (so the window slides inward at the ends and
@@ -108,7 +113,8 @@ int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out);
  *
  * Arguments (all host memory, caller-owned):
  *   T >= 1 frames, C >= 2 budget, 1 <= W <= C-1 window, step >= 0, flags one
- *   of LVSA_ROT_MOD_TPER / LVSA_ROT_MOD_T / LVSA_FIXED_GRID.
+ *   of LVSA_ROT_MOD_TPER / LVSA_ROT_MOD_T / LVSA_FIXED_GRID /
+ *   LVSA_WINDOW_ONLY.
  *   row_ptr [T+1] out: row_ptr[t] = t * c_eff.
  *   col_idx [cap] out: rows concatenated, each ascending and unique.
  *   info    out, may be NULL.

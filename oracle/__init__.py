@@ -35,6 +35,7 @@ from .mask import (  # noqa: F401
     ROT_MOD_TPER,
     ROT_MOD_T,
     FIXED_GRID,
+    WINDOW_ONLY,
     MaskInfo,
     validate,
     schedule,

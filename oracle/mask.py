@@ -58,6 +58,9 @@ ROT_MOD_TPER = 0  # default rotation: offset = s mod Tper   (R3, [gist])
 ROT_MOD_T = 1     # rotation variant: offset = s mod T      (R3, [tw3])
 FIXED_GRID = 2    # ablation: anchors never move (offset 0; the grid the
                   # pages name as the source of fixed-grid bias)
+WINDOW_ONLY = 3   # ablation: no anchors, the C frames nearest to t (plain
+                  # sliding-window attention, the prior-art pattern the pages
+                  # contrast LVSA with)
 
 
 class OracleArgError(ValueError):
@@ -90,7 +93,7 @@ def validate(T: int, C: int, W: int, step: int, flags: int = ROT_MOD_TPER) -> No
         raise OracleArgError("W must satisfy 1 <= W <= C-1")
     if step < 0:
         raise OracleArgError("step must be >= 0")
-    if flags not in (ROT_MOD_TPER, ROT_MOD_T, FIXED_GRID):
+    if flags not in (ROT_MOD_TPER, ROT_MOD_T, FIXED_GRID, WINDOW_ONLY):
         raise OracleArgError("unknown flags value")
 
 
@@ -126,7 +129,7 @@ def anchors(T: int, C: int, W: int, step: int, flags: int = ROT_MOD_TPER) -> Lis
     Empty in the dense case T ≤ C (every frame is attended anyway).
     """
     validate(T, C, W, step, flags)
-    if T <= C:
+    if T <= C or flags == WINDOW_ONLY:
         return []
     t_per, n_g = schedule(T, C, W)
     o = anchor_offset(T, t_per, step, flags)
@@ -189,7 +192,7 @@ def build_mask(T: int, C: int, W: int, step: int, flags: int = ROT_MOD_TPER):
     for r in rows:
         col_idx.extend(r)
         row_ptr.append(len(col_idx))
-    if T <= C:
+    if T <= C or flags == WINDOW_ONLY:
         info = MaskInfo(c_eff=c_eff, t_per=0, n_anchor=0, offset=0, nnz=len(col_idx))
     else:
         t_per, n_g = schedule(T, C, W)

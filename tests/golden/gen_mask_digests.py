@@ -36,7 +36,7 @@ def digest(row_ptr, col_idx):
 def lines():
     out = []
     for name, T, C, W, n in SHAPES:
-        for flags in (om.ROT_MOD_TPER, om.ROT_MOD_T, om.FIXED_GRID):
+        for flags in (om.ROT_MOD_TPER, om.ROT_MOD_T, om.FIXED_GRID, om.WINDOW_ONLY):
             for s in range(n):
                 rp, ci, _ = om.build_mask(T, C, W, s, flags)
                 out.append(f"{name} {T} {C} {W} {flags} {s} {digest(rp, ci)}")

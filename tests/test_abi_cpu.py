@@ -45,7 +45,7 @@ def _lib_rows(T, C, W, s, flags):
     return m, m.rows()
 
 
-@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T, L.LVSA_FIXED_GRID])
+@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T, L.LVSA_FIXED_GRID, L.LVSA_WINDOW_ONLY])
 def test_mask_bit_exact_at_workload_shapes(flags):
     for T, C, W, n in [(8, 4, 2, 8), (21, 21, 9, 50), (121, 21, 9, 50), (49, 33, 13, 50), (65, 33, 13, 50)]:
         for s in range(n):

@@ -63,7 +63,7 @@ def run_lib(q, k, v, T, C, W, step, flags=L.LVSA_ROT_MOD_TPER, scale=None, out=N
 # ------------------------------------------------ tiny workload, full output --
 
 
-@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T, L.LVSA_FIXED_GRID])
+@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T, L.LVSA_FIXED_GRID, L.LVSA_WINDOW_ONLY])
 def test_tiny_all_steps_full_output(gpu, flags):
     w = WORKLOADS["tiny"]
     say("tiny", w, "flags", flags)
@@ -104,6 +104,8 @@ def test_mid_size_full_output(gpu, case):
             o, rows = run_lib(qd, kd, vd, T, C, W, s, flags)
             ref = oa.block_attention(q, k, v, rows)
             assert_close(o, ref, f"mid {case} step {s} flags {flags}")
+    o, rows = run_lib(qd, kd, vd, T, C, W, 2, L.LVSA_WINDOW_ONLY)
+    assert_close(o, oa.block_attention(q, k, v, rows), f"mid {case} window-only")
 
 
 def test_strided_inputs_and_explicit_scale(gpu):

@@ -289,3 +289,28 @@ def test_mutation_anchor_positions_not_wrapped(monkeypatch):
         return [f for f in orig_anchors(T, C, W, step, flags) if f >= (step % max(1, om.schedule(T, C, W)[0]) if T > C else 0)]
     monkeypatch.setattr(om, "anchors", anchors)
     assert not _all_pins()
+
+
+def window_only_closed_form(T, C, t):
+    """Sliding window of min(C, T) frames centred on t (lower side first on
+    ties), slid inward at the sequence ends."""
+    n = min(C, T)
+    lo = t - (n // 2)
+    hi = lo + n - 1
+    if lo < 0:
+        lo, hi = 0, n - 1
+    if hi > T - 1:
+        lo, hi = T - n, T - 1
+    return list(range(lo, hi + 1))
+
+
+def test_window_only_ablation_is_a_sliding_window():
+    for T in (1, 2, 5, 8, 21, 49, 121):
+        for C in (2, 3, 4, 21, 33):
+            for W in sorted({1, C - 1}):
+                rows = om.key_frames(T, C, W, 3, om.WINDOW_ONLY)
+                assert om.anchors(T, C, W, 3, om.WINDOW_ONLY) == []
+                for t in range(T):
+                    assert rows[t] == window_only_closed_form(T, C, t), (T, C, t)
+    # the window does not move with the step
+    assert om.key_frames(121, 21, 9, 0, om.WINDOW_ONLY) == om.key_frames(121, 21, 9, 17, om.WINDOW_ONLY)
