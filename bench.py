@@ -113,6 +113,7 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False):
 
     dev = torch.device("cuda:0")
     lib = L.library()
+    torch.cuda.synchronize(dev)  # initialises the device before the memory statistics are reset
     torch.cuda.reset_peak_memory_stats(dev)
     q, k, v = make_qkv(w, device=dev)
     out = torch.empty_like(q)
