@@ -8,17 +8,23 @@
 // per-query cost O(C·P·d) -- the sparsity block is a whole frame of P
 // tokens).
 //
-// Work decomposition.  One workgroup = one tile of BM query tokens of one
-// frame t of one (b, h); NW wavefronts of 64 lanes each own 32 query rows.
-// The workgroup walks its CSR row once, merging consecutive key frames into
-// runs: tokens are frame-major, so a run of frames [f0, f1] is the one
-// contiguous token range [f0·P, (f1+1)·P).  Each run is streamed in tiles of
-// BN = 64 keys; only the last tile of a run is partial (P = 1560 is not a
-// multiple of the MFMA tile, so that tail is masked).
+// Work decomposition.  One workgroup = one tile of BM = 32·NW query tokens
+// of one frame t of one (b, h); each of its NW wavefronts owns 32 query
+// rows.  The last tile of a frame is partial when BM does not divide P (Wan
+// latents: P = 1560 = 12·128 + 24); its idle waves only join the loads and
+// barriers, and the SIMDs they sit on run the other resident workgroups'
+// waves meanwhile (packing the remainders of several frames into one tile
+// measured slower: the merged iteration costs more than the idle waves).
+//
+// Key iteration.  The workgroup walks its CSR row once, merging consecutive
+// key frames into runs: tokens are frame-major, so a run of frames [f0, f1]
+// is the one contiguous token range [f0·P, (f1+1)·P).  Each run is streamed
+// in tiles of BN keys; only the last tile of a run is partial, and its
+// missing keys are masked.
 //
 // Per key tile, per wave (all on the matrix cores, bf16 -> fp32):
 //   Sᵀ(32 keys × 32 queries) = K · Qᵀ    v_mfma_f32_32x32x16_bf16, K from LDS,
-//                                         Q held in VGPRs for the whole tile.
+//                                         Q held in VGPRs for the whole loop.
 //   In the 32x32 accumulator layout lane l holds query l%32 and keys
 //   8i + 4(l/32) + j, so a query's row lives in lanes l and l^32: the row
 //   max and sum are per-lane reductions plus one permlane32 swap.
@@ -26,13 +32,15 @@
 //   (rescale only when the tile max exceeds it by more than 2^8, so exp2
 //   arguments stay <= 8 and fp32 cannot overflow).
 //   Oᵀ(d × 32 queries) += Vᵀ · Pᵀ         P (bf16) comes straight from the Sᵀ
-//   accumulator registers; Vᵀ is staged transposed in LDS.
+//                                         accumulator registers; the Vᵀ
+//                                         operand is built by transposing
+//                                         LDS reads (ds_read_b64_tr_b16).
 //
-// K/V staging.  Global -> registers (16-byte loads, issued one tile ahead)
-// -> LDS, double-buffered, one workgroup barrier per tile.  K rows are
-// stored with a 16-byte pad (row pitch 272 B for d = 128) so the 16-byte
-// MFMA-operand reads are conflict-free; V is written transposed (Vᵀ[d][key],
-// pitch 136 B) so each lane's 8-key operand is two 8-byte reads.
+// K/V staging.  Each tile's K and V rows go from global memory straight into
+// LDS (buffer loads with the LDS-destination bit, 16 bytes per lane), double
+// buffered: the loads of tile j+1 run while tile j is computed, one
+// workgroup barrier per tile.  16-byte chunks are XOR-swizzled by key so
+// every MFMA operand read is bank-conflict free.
 //
 // Launch order.  Workgroups are dispatched round-robin over the 8 XCDs; the
 // block index is remapped so each XCD receives a contiguous range of
@@ -45,7 +53,6 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
-#include <type_traits>
 
 #include "lvsa_internal.h"
 
@@ -72,9 +79,6 @@ typedef uint16_t u16;
 #ifndef LVSA_QB
 #define LVSA_QB 1
 #endif
-#ifndef LVSA_STAGES
-#define LVSA_STAGES 2
-#endif
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
@@ -90,18 +94,22 @@ struct Args {
 };
 
 // Walks one CSR row and yields maximal runs of consecutive frames as token
-// ranges [ks, ke).  Every value is wave-uniform (scalar registers).
+// ranges [ks, ke).  Every value is wave-uniform (scalar registers).  An entry
+// outside [0, T), or not above the last frame taken, is skipped, so a
+// malformed row never causes an out-of-range read and never repeats a frame.
 struct RunIter {
   const int32_t *cols;
   int32_t e, e_end, T, P;
+  int32_t last;  // last frame taken (-1 before the first)
   int32_t ks, ke;
 
   __device__ bool next_run() {
     while (e < e_end) {
       const int32_t f = cols[e++];
-      if (f < 0 || f >= T) continue;  // malformed entry: skipped, never read
+      if (f <= last || f >= T) continue;
       int32_t f1 = f;
       while (e < e_end && f1 + 1 < T && cols[e] == f1 + 1) { ++f1; ++e; }
+      last = f1;
       ks = f * P;
       ke = (f1 + 1) * P;
       return true;
@@ -147,7 +155,7 @@ struct Cfg {
   static constexpr int LOADS_PER_WAVE = LOADS / NW;
   static constexpr int VSW = CH / 4;          // V swizzle step
   static constexpr int KEYS_PER_LOAD = 64 / CH;       // keys per 1 KB wave load
-  static constexpr int STAGES = LVSA_STAGES;          // LDS tile buffers (loads run STAGES-1 tiles ahead)
+  static constexpr int STAGES = 2;                    // LDS tile buffers (loads run one tile ahead)
   static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES; // {K, V} × STAGES
   static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
 };
@@ -413,72 +421,10 @@ void lvsa_attn_fwd(Args a) {
     it.e_end = re;
     it.T = a.T;
     it.P = P;
+    it.last = -1;
     it.ks = it.ke = 0;
   }
 
-#if LVSA_STAGES == 3
-  // ---- main loop over key tiles: K and V triple-buffered in LDS (tile j in
-  // buffer j mod 3); the loads of tile j+2 are issued before tile j is
-  // computed, and each tile's end waits only for tile j+1's loads; one
-  // barrier per tile.  Unrolled by three so that every LDS offset is an
-  // immediate.
-  int n_tiles = 0;
-  {
-    RunIter c = it;
-    while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
-  }
-  int pos = 0, kv = 0;
-  auto advance = [&]() {  // next tile, moving to the next run when needed
-    pos += C::BN;
-    if (pos >= it.ke) {
-      it.next_run();
-      pos = it.ks;
-    }
-    kv = min(C::BN, it.ke - pos);
-  };
-  auto issue = [&](int buf) {
-    blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
-    blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
-  };
-  int kvq0 = 0, kvq1 = 0;  // valid keys of the next two tiles to compute
-  if (n_tiles > 0) {
-    it.next_run();
-    pos = it.ks;
-    kv = min(C::BN, it.ke - pos);
-    issue(0);
-    kvq0 = kv;
-  }
-  if (n_tiles > 1) {
-    advance();
-    issue(1);
-    kvq1 = kv;
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS_PER_WAVE) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-  // step: compute tile j (buffer B) while tile j+2 loads into buffer (B+2)%3
-  auto step = [&](auto bufc, int j) {
-    constexpr int B = decltype(bufc)::value;
-    const int kvj = kvq0;
-    kvq0 = kvq1;
-    const bool more = j + 2 < n_tiles;
-    if (more) {
-      advance();
-      issue((B + 2) % 3);
-      kvq1 = kv;
-    }
-    if (any_live) blk.template tile<B>(kvj);
-    if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * C::LOADS_PER_WAVE) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-  for (int j = 0; j < n_tiles; j += 3) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
-    if (j + 2 < n_tiles) step(std::integral_constant<int, 2>{}, j + 2);
-  }
-#else
   // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
   // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
   // barrier per tile.  Unrolled by two so that every LDS offset is an
@@ -526,8 +472,6 @@ void lvsa_attn_fwd(Args a) {
     __syncthreads();
   }
   if ((n_tiles & 1) && any_live) blk.template tile<0>(kv);
-
-#endif
 
   // ---- epilogue: normalise, round to bf16, store
 #pragma unroll

@@ -149,10 +149,11 @@ int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx
  *   row_ptr_dev  : [T+1] int32 device array, CSR row offsets into col_idx.
  *   col_idx_dev  : [nnz] int32 device array, key frames of each query frame,
  *                  ascending and unique per row (lvsa_build_mask's output
- *                  copied to the device).  Entries outside [0, T) are
- *                  skipped and offsets are clamped to [0, nnz], so a
+ *                  copied to the device).  An entry outside [0, T), or not
+ *                  above the last entry kept before it in its row, is
+ *                  skipped, and offsets are clamped to [0, nnz], so a
  *                  malformed mask gives wrong numbers, never an
- *                  out-of-bounds access; a row with no valid frame yields
+ *                  out-of-bounds access; a row with no kept frame yields
  *                  zeros.
  *   T            : frames (N % T must be 0).
  *   nnz          : length of col_idx_dev.

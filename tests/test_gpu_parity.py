@@ -81,11 +81,11 @@ def test_tiny_all_steps_full_output(gpu, flags):
 
 MID_CASES = [
     # (B, H, T, P, d, C, W, seed)
-    (2, 3, 12, 200, 128, 5, 2, 101),   # 2 query tiles (128 + 72), 3 key tiles + 8-key tail
-    (1, 2, 9, 1560, 128, 4, 2, 102),   # real frame size, 13 query tiles, 25 key tiles/frame
+    (2, 3, 12, 200, 128, 5, 2, 101),   # 2 query tiles (128 + 72), 6 key tiles + 8-key tail
+    (1, 2, 9, 1560, 128, 4, 2, 102),   # real frame size: 13 query tiles (last 24 rows), 49 key tiles
     (1, 4, 16, 37, 64, 6, 3, 103),     # frames smaller than one key tile
     (1, 2, 10, 1, 128, 3, 1, 104),     # one token per frame
-    (2, 2, 7, 129, 64, 7, 3, 105),     # C = T: dense, one run of 903 keys
+    (2, 2, 7, 129, 64, 7, 3, 105),     # C = T: dense, one run of 903 keys; 1-row last tile
     (1, 1, 1, 300, 128, 4, 2, 106),    # a single frame
     (1, 3, 20, 64, 128, 9, 4, 107),    # key tiles exactly aligned to frames
 ]
@@ -148,14 +148,27 @@ def test_custom_csr_masks(gpu):
     assert_close(o, oa.block_attention(q, k, v, rows), "custom csr")
 
 
+def kept_entries(row, T):
+    """The entries of a raw CSR row the kernel uses: in [0, T) and above the
+    last entry kept before them (a malformed row never reads out of range)."""
+    out = []
+    for f in row:
+        if (out[-1] if out else -1) < f < T:
+            out.append(f)
+    return out
+
+
 def test_malformed_mask_entries_are_skipped_and_empty_rows_give_zeros(gpu):
-    B, H, T, P, d = 1, 1, 6, 70, 64
+    # Out-of-range, empty, descending and repeated entries; P = 150 gives a
+    # full and a partial query tile per frame.
+    B, H, T, P, d = 1, 1, 8, 150, 64
     say("malformed mask", (B, H, T, P, d))
     q = make_random((B, H, T * P, d), 401)
     k = make_random((B, H, T * P, d), 402)
     v = make_random((B, H, T * P, d), 403)
-    raw = [[0, 1], [-3, 2, 99], [], [4, 5, 6], [1000], [5]]
-    rows = [[f for f in r if 0 <= f < T] for r in raw]
+    raw = [[0, 1], [-3, 2, 99], [], [4, 5, 6], [1000], [5], [3, 1, 3, 4], [2, 2, 0, 7, 6]]
+    rows = [kept_entries(r, T) for r in raw]
+    assert rows[6] == [3, 4] and rows[7] == [2, 7]
     rp = [0]
     ci = []
     for r in raw:
