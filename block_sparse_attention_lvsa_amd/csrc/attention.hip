@@ -409,6 +409,9 @@ void lvsa_attn_fwd(Args a) {
     blk.l_run[q] = 0.f;
   }
   blk.init_offsets(a.k_sn, a.v_sn);
+  // Scalar copy of the wave-uniform flag, so the per-tile test is a scalar
+  // branch rather than a vector compare.
+  const int compute = __builtin_amdgcn_readfirstlane(any_live ? 1 : 0);
 
   // ---- CSR row -> runs of key frames
   RunIter it;
@@ -459,7 +462,7 @@ void lvsa_attn_fwd(Args a) {
     const int kv0 = kv;
     advance();  // tile i+1 -> buffer 1
     issue(1);
-    if (any_live) blk.template tile<0>(kv0);
+    if (compute) blk.template tile<0>(kv0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int kv1 = kv;
@@ -467,11 +470,11 @@ void lvsa_attn_fwd(Args a) {
       advance();
       issue(0);
     }
-    if (any_live) blk.template tile<1>(kv1);
+    if (compute) blk.template tile<1>(kv1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if ((n_tiles & 1) && any_live) blk.template tile<0>(kv);
+  if ((n_tiles & 1) && compute) blk.template tile<0>(kv);
 
   // ---- epilogue: normalise, round to bf16, store
 #pragma unroll
@@ -572,7 +575,11 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   if (q->N > INT32_MAX / 2) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld too large", (long long)q->N);
   if (!row_ptr_dev || !col_idx_dev || nnz < 0)
     return lvsa::fail(LVSA_ERR_ARG, "row_ptr/col_idx NULL or nnz < 0");
-  if (!(scale == scale) || std::isinf(scale)) return lvsa::fail(LVSA_ERR_ARG, "scale is not finite");
+  {
+    uint32_t bits;  // exponent all ones: inf or NaN (a bit test no fast-math flag can fold)
+    std::memcpy(&bits, &scale, sizeof bits);
+    if ((bits & 0x7f800000u) == 0x7f800000u) return lvsa::fail(LVSA_ERR_ARG, "scale is not finite");
+  }
   int dev;
   if ((rc = check_device(&dev))) return rc;
 
