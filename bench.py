@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "LVSA attention effective TFLOP/s + ms/call, T=121×1560 tok, H=12 d=128 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_wan13b_6x.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_lvsa_amd", "csrc", "attention.hip")]
-SWEEP = ["wan13b_1x", "syn_1p5x", "syn_2x", "wan13b_6x", "wan14b_6x"]
+SWEEP = ["wan13b_1x", "syn_1p5x", "syn_2x", "wan13b_6x", "wan14b_6x", "wan22_720p_6x_h5", "wan13b_720p_6x"]
 
 
 def log(*a):

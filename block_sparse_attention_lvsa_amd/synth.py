@@ -16,6 +16,15 @@ frame; horizons 1× and 6× of Wan 2.1 (21 and 121 latent frames); 1.5× and 2×
   wan14b_6x   1  40 128  121  1560  21  9   4     iid N(0,1) + per-frame N(0,0.5²)
   syn_1p5x    1  16 128  49   1560  33  13  5     iid N(0,1)
   syn_2x      1  16 128  65   1560  33  13  6     iid N(0,1)
+  wan13b_720p_6x  1 12 128 121 3600 21 9  7     iid N(0,1)
+  wan22_720p_6x_h5 1 5 128 121 3600 21 9  8     iid N(0,1) + per-frame N(0,0.5²)
+
+The two 720p workloads take the pages' 720×1280 runs (TechWalker article,
+§五) with the latent grid assumed to shrink as at 480×832 (×8 spatially by
+the VAE, ×2 by the patch embedding: 45×80 = 3600 tokens per latent frame).
+``wan22_720p_6x_h5`` is one device's share of the Wan 2.2-A14B run, whose 40
+heads the pages split over 8 devices by sequence parallelism: 5 heads at the
+full sequence length.
 
 Recipe: ``torch.Generator(device).manual_seed(seed)``; ``torch.randn`` in
 float32 drawn in the order q, k, v (then the per-frame components z_q, z_k,
@@ -59,6 +68,8 @@ WORKLOADS = {
     "wan14b_6x": Workload("wan14b_6x", 1, 40, 128, 121, 1560, 21, 9, 4, frame_std=0.5),
     "syn_1p5x": Workload("syn_1p5x", 1, 16, 128, 49, 1560, 33, 13, 5),
     "syn_2x": Workload("syn_2x", 1, 16, 128, 65, 1560, 33, 13, 6),
+    "wan13b_720p_6x": Workload("wan13b_720p_6x", 1, 12, 128, 121, 3600, 21, 9, 7),
+    "wan22_720p_6x_h5": Workload("wan22_720p_6x_h5", 1, 5, 128, 121, 3600, 21, 9, 8, frame_std=0.5),
 }
 
 

@@ -258,16 +258,22 @@ FULL = [
     ("wan14b_6x", (0, 11), (L.LVSA_ROT_MOD_TPER,)),
     ("syn_1p5x", (0, 1, 2, 3, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T)),
     ("syn_2x", (0, 1, 3, 4, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T)),
+    ("wan22_720p_6x_h5", (0, 10, 11), (L.LVSA_ROT_MOD_TPER,)),
+    ("wan13b_720p_6x", (0, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_FIXED_GRID)),
 ]
 
 
 def sample_tokens(T, P, rnd, n_rand=12):
+    """Structured tokens (frame starts and ends, 128-row query-tile edges, the
+    first row of a frame's partial last tile) of four frames, plus random ones."""
+    last_tile = (P // 128) * 128
     toks = set()
     for t in (0, 1, T // 2, T - 1):
-        for p in (0, 1, 127, 128, 255, 256, P - 25, P - 24, P - 1):
+        for p in (0, 1, 127, 128, 255, 256, last_tile - 1, last_tile, P - 25, P - 24, P - 1):
             if 0 <= p < P:
                 toks.add(t * P + p)
-    while len(toks) < 36 + n_rand:  # 36 structured tokens (4 frames × 9 positions)
+    n_structured = len(toks)
+    while len(toks) < n_structured + n_rand:
         toks.add(rnd.randrange(T * P))
     return sorted(toks)
 
