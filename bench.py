@@ -16,8 +16,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same step
   also          per-call kernel median/p10/p90, host mask build and mask H2D
                 times, dense comparator (same kernel, C = T mask) and speedup,
-                peak device memory; for workloads at the training horizon
-                (T <= C) the full-step / dense-kernel time ratio.
+                peak device memory; the same steps with every mask built
+                ahead of time (one launch per step, and one HIP-graph replay
+                of the whole sequence); for workloads at the training horizon
+                (T <= C) the full-step / dense-kernel time ratios.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan13b_6x]
     python bench.py --sweep [--sweep-out FILE]   # every workload, table on stderr
@@ -105,7 +107,7 @@ def pct(xs, p):
     return xs[min(len(xs) - 1, int(p * len(xs)))]
 
 
-def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False):
+def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, modes=True):
     """Times `steps` full hot-path steps of workload `w`; returns a dict."""
     import torch
     import block_sparse_attention_lvsa_amd as L
@@ -198,6 +200,42 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False):
         "mask_h2d_ms_median": statistics.median(h2d),
         "flops_per_step": flops,
     }
+    if modes:
+        # The same steps with no per-step host work: all masks built ahead of
+        # time and copied once (outside the timed region), then (a) one launch
+        # per step, (b) the whole step sequence replayed from a HIP graph.
+        ms = L.lvsa_build_mask_steps(T, C, W, 0, steps).to(dev)
+        torch.cuda.synchronize()
+
+        def launch_all():
+            sptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            for j in range(steps):
+                rc = lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
+                                        ctypes.c_void_p(ms.row_ptr.data_ptr()),
+                                        ctypes.c_void_p(ms.col_idx[j].data_ptr()),
+                                        T, nnz, ctypes.byref(recs[3]), 0.0, sptr)
+                if rc:
+                    raise RuntimeError(L.lvsa_last_error())
+
+        def timed(fn):
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            g0.record(stream)
+            fn()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            return max(g0.elapsed_time(g1), (time.perf_counter() - w0) * 1e3) / steps
+
+        launch_all()
+        prebuilt_ms = timed(launch_all)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            launch_all()
+        graph.replay()
+        graph_ms = timed(graph.replay)
+        res["step_modes_ms"] = {"host_mask_each_step": ms_per_step, "prebuilt_masks": prebuilt_ms,
+                                "graph_replay": graph_ms, "kernel_only_avg": k_avg}
+        del graph
     if dense:
         # Dense comparator: the same kernel with a C = T mask (one run of N keys).
         dm = L.lvsa_build_mask(T, max(T, 2), 1, 0).to(dev)
@@ -219,6 +257,8 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False):
             # At the training horizon the method is the dense model: the full
             # step (host mask + H2D + kernel) against the dense kernel alone.
             res["full_step_over_dense_kernel"] = ms_per_step / dense_ms
+            if modes:
+                res["graph_step_over_dense_kernel"] = res["step_modes_ms"]["graph_replay"] / dense_ms
     res["max_memory_allocated_gb"] = torch.cuda.max_memory_allocated(dev) / 1e9
     if keep_inputs:
         res["_inputs"] = (q, k, v)
@@ -234,6 +274,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-step-modes", action="store_true",
+                    help="skip the prebuilt-mask and graph-replay timings of the same steps")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
     ap.add_argument("--sweep", action="store_true", help="time every workload (table on stderr)")
@@ -249,18 +291,22 @@ def main():
 
     if args.sweep:
         lines = ["| workload | B·H, T×P, C/W | ms/call (median) | effective TFLOP/s | % of 2.5 PF | dense (C=T) ms | "
-                 "speedup | ideal T/C | full step / dense (T≤C) | peak mem GB |",
-                 "|---|---|---|---|---|---|---|---|---|---|"]
+                 "speedup | ideal T/C | ms/step: host mask each step / prebuilt / graph | "
+                 "full step / dense (T≤C): host mask / graph | peak mem GB |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|"]
         for name in SWEEP:
             w = WORKLOADS[name]
             r = run_workload(w, args.steps, args.warmup, dense=True)
             log(json.dumps(r))
             ov = r.get("full_step_over_dense_kernel")
+            og = r.get("graph_step_over_dense_kernel")
+            sm = r["step_modes_ms"]
             lines.append(f"| {name} | {w.B * w.H}, {w.T}×{w.P}, {w.C}/{w.W} | {r['kernel_ms']['median']:.3f} | "
                          f"{r['kernel_tflops']:.1f} | {100 * r['kernel_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
                          f"{r['dense_ms_per_call']:.3f} | {r['speedup_vs_dense_kernel']:.2f} | "
-                         f"{r['ideal_speedup_T_over_C']:.2f} | {'%.3f' % ov if ov else '—'} | "
-                         f"{r['max_memory_allocated_gb']:.1f} |")
+                         f"{r['ideal_speedup_T_over_C']:.2f} | {sm['host_mask_each_step']:.3f} / "
+                         f"{sm['prebuilt_masks']:.3f} / {sm['graph_replay']:.3f} | "
+                         f"{'%.3f / %.3f' % (ov, og) if ov else '—'} | {r['max_memory_allocated_gb']:.1f} |")
             torch.cuda.empty_cache()
         table = "\n".join(lines)
         log(table)
@@ -272,12 +318,16 @@ def main():
     w = WORKLOADS[args.workload]
     log(f"workload {w}")
     r = run_workload(w, args.steps, args.warmup, dense=not args.no_dense, calib_copy=args.calib_copy,
-                     keep_inputs=not args.no_cpu_baseline)
+                     keep_inputs=not args.no_cpu_baseline, modes=not args.no_step_modes)
     log(f"step: {r['ms_per_step']:.3f} ms  kernel avg {r['kernel_ms']['avg']:.3f} ms (median "
         f"{r['kernel_ms']['median']:.3f}, p10 {r['kernel_ms']['p10']:.3f}, p90 {r['kernel_ms']['p90']:.3f})  "
         f"{r['value']:.1f} TFLOP/s effective, kernel {r['kernel_tflops']:.1f} TFLOP/s")
     log(f"host mask build: median {r['mask_build_us_median']:.1f} us/step; mask H2D median "
         f"{r['mask_h2d_ms_median'] * 1e3:.1f} us/step")
+    if "step_modes_ms" in r:
+        sm = r["step_modes_ms"]
+        log(f"ms/step: host mask each step {sm['host_mask_each_step']:.3f}, masks prebuilt {sm['prebuilt_masks']:.3f}, "
+            f"graph replay {sm['graph_replay']:.3f} (kernel alone {sm['kernel_only_avg']:.3f})")
     if "dense_ms_per_call" in r:
         log(f"dense (C=T) kernel: {r['dense_ms_per_call']:.3f} ms -> speedup {r['speedup_vs_dense_kernel']:.2f}x "
             f"(ideal {r['ideal_speedup_T_over_C']:.2f}x)")
@@ -296,8 +346,10 @@ def main():
 
     extra = {key: (round(val, 4) if isinstance(val, float) else val) for key, val in r.items()
              if key in ("dense_ms_per_call", "speedup_vs_dense_kernel", "ideal_speedup_T_over_C",
-                        "full_step_over_dense_kernel", "mask_build_us_median", "mask_h2d_ms_median",
-                        "max_memory_allocated_gb")}
+                        "full_step_over_dense_kernel", "graph_step_over_dense_kernel", "mask_build_us_median",
+                        "mask_h2d_ms_median", "max_memory_allocated_gb")}
+    if "step_modes_ms" in r:
+        extra["step_modes_ms"] = {key: round(val, 4) for key, val in r["step_modes_ms"].items()}
     extra["kernel_ms"] = {key: round(val, 4) for key, val in r["kernel_ms"].items()}
     rec = {
         "metric": METRIC,

@@ -14,11 +14,14 @@ Functions with the ABI's names:
   lvsa_last_error()                   -> str
   lvsa_mask_nnz(T, C, W)              -> int
   lvsa_build_mask(T, C, W, step, flags=LVSA_ROT_MOD_TPER) -> Mask (host int32)
+  lvsa_build_mask_steps(T, C, W, step0, n_steps, flags=...) -> MaskSteps (host int32)
   lvsa_validate_mask(T, row_ptr, col_idx)
   lvsa_attention(q, k, v, mask_dev, out=None, scale=None, stream=None) -> out
 
 ``Mask.to(device)`` copies the CSR arrays (``non_blocking`` on the current
-stream) for ``lvsa_attention``.
+stream) for ``lvsa_attention``.  ``MaskSteps`` holds the masks of a run of
+steps in one buffer: ``.to(device)`` copies them all at once and
+``.mask(i)`` is the ``Mask`` of step step0+i (views, no copy).
 """
 
 from __future__ import annotations
@@ -92,6 +95,9 @@ def library() -> ctypes.CDLL:
         lib.lvsa_build_mask.restype = ctypes.c_int
         lib.lvsa_build_mask.argtypes = [ctypes.c_int32] * 5 + [_I32P, _I32P, ctypes.c_int32,
                                                                 ctypes.POINTER(LvsaMaskInfo)]
+        lib.lvsa_build_mask_steps.restype = ctypes.c_int
+        lib.lvsa_build_mask_steps.argtypes = [ctypes.c_int32] * 6 + [_I32P, _I32P, ctypes.c_int64,
+                                                                      ctypes.POINTER(LvsaMaskInfo)]
         lib.lvsa_validate_mask.restype = ctypes.c_int
         lib.lvsa_validate_mask.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32]
         lib.lvsa_attention.restype = ctypes.c_int
@@ -161,6 +167,46 @@ def lvsa_build_mask(T: int, C: int, W: int, step: int, flags: int = LVSA_ROT_MOD
     _check(library().lvsa_build_mask(T, C, W, step, flags, _i32ptr(row_ptr), _i32ptr(col_idx),
                                      nnz, ctypes.byref(info)))
     return Mask(row_ptr, col_idx[:nnz], T, info.c_eff, info.t_per, info.n_anchor, info.offset, info.nnz)
+
+
+class MaskSteps(NamedTuple):
+    """CSR masks of steps step0 .. step0+n_steps-1 sharing one row_ptr [T+1];
+    col_idx is [n_steps, nnz] (int32).  ``info[i]`` = (c_eff, t_per,
+    n_anchor, offset) of step step0+i."""
+    row_ptr: "object"
+    col_idx: "object"
+    T: int
+    step0: int
+    n_steps: int
+    nnz: int
+    info: tuple
+
+    def to(self, device, non_blocking: bool = True) -> "MaskSteps":
+        return self._replace(row_ptr=self.row_ptr.to(device, non_blocking=non_blocking),
+                             col_idx=self.col_idx.to(device, non_blocking=non_blocking))
+
+    def mask(self, i: int) -> Mask:
+        if not 0 <= i < self.n_steps:
+            raise IndexError(f"step index {i} outside [0, {self.n_steps})")
+        c_eff, t_per, n_anchor, offset = self.info[i]
+        return Mask(self.row_ptr, self.col_idx[i], self.T, c_eff, t_per, n_anchor, offset, self.nnz)
+
+
+def lvsa_build_mask_steps(T: int, C: int, W: int, step0: int, n_steps: int,
+                          flags: int = LVSA_ROT_MOD_TPER, pin_memory: bool = False) -> MaskSteps:
+    """Host CSR masks of n_steps consecutive denoising steps in one buffer
+    (C++ builder; see include/lvsa.h)."""
+    import torch
+    nnz = lvsa_mask_nnz(T, C, W)
+    if n_steps < 1:
+        raise LvsaValueError(LVSA_ERR_ARG, f"n_steps={n_steps}: need n_steps >= 1")
+    row_ptr = torch.empty(T + 1, dtype=torch.int32, pin_memory=pin_memory)
+    col_idx = torch.empty(n_steps, nnz, dtype=torch.int32, pin_memory=pin_memory)
+    infos = (LvsaMaskInfo * n_steps)()
+    _check(library().lvsa_build_mask_steps(T, C, W, step0, n_steps, flags, _i32ptr(row_ptr), _i32ptr(col_idx),
+                                           n_steps * nnz, infos))
+    info = tuple((x.c_eff, x.t_per, x.n_anchor, x.offset) for x in infos)
+    return MaskSteps(row_ptr, col_idx, T, step0, n_steps, nnz, info)
 
 
 def lvsa_validate_mask(T: int, row_ptr, col_idx) -> None:

@@ -121,6 +121,36 @@ extern "C" int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, in
   return lvsa::ok();
 }
 
+extern "C" int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps,
+                                     int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                                     lvsa_mask_info *info) {
+  if (n_steps < 1) return lvsa::fail(LVSA_ERR_ARG, "n_steps=%d: need n_steps >= 1", n_steps);
+  int rc = check_domain(T, C, W, step0, flags);
+  if (rc) return rc;
+  if ((int64_t)step0 + n_steps - 1 > INT32_MAX)
+    return lvsa::fail(LVSA_ERR_ARG, "step0 + n_steps - 1 exceeds int32");
+  if (!row_ptr || !col_idx) return lvsa::fail(LVSA_ERR_ARG, "row_ptr/col_idx is NULL");
+  const int64_t nnz = nnz_of(T, C);
+  if (nnz > INT32_MAX) return lvsa::fail(LVSA_ERR_ARG, "mask of %lld entries exceeds int32", (long long)nnz);
+  if (cap < nnz * n_steps)
+    return lvsa::fail(LVSA_ERR_CAPACITY, "col_idx capacity %lld < required %lld", (long long)cap,
+                      (long long)(nnz * n_steps));
+  // Every step's row offsets are the same (t * c_eff), so the first call
+  // writes row_ptr and the others only their own block of col_idx.
+  for (int32_t i = 0; i < n_steps; ++i) {
+    int32_t *rp = i == 0 ? row_ptr : nullptr;
+    std::vector<int32_t> scratch_rp;
+    if (!rp) {
+      scratch_rp.resize(T + 1);
+      rp = scratch_rp.data();
+    }
+    rc = lvsa_build_mask(T, C, W, step0 + i, flags, rp, col_idx + (int64_t)i * nnz, (int32_t)nnz,
+                         info ? info + i : nullptr);
+    if (rc) return rc;
+  }
+  return lvsa::ok();
+}
+
 extern "C" int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx,
                                   int32_t nnz) {
   if (T < 1 || nnz < 0) return lvsa::fail(LVSA_ERR_ARG, "T=%d nnz=%d out of domain", T, nnz);

@@ -124,6 +124,27 @@ int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags
                     int32_t *row_ptr, int32_t *col_idx, int32_t cap,
                     lvsa_mask_info *info);
 
+/* Host mask builder for a run of denoising steps: the masks of steps
+ * step0 .. step0+n_steps-1, as lvsa_build_mask builds them, in one buffer, so
+ * that a whole sampling run's masks can be copied to the device once and the
+ * step sequence launched (or captured in a HIP graph) with no per-step host
+ * work.  (The pages put the mask on the CPU every step -- TechWalker article,
+ * §二 and §三 -- and name per-step pattern scheduling as the overhead that
+ * keeps short sequences from gaining -- same article, §五.)
+ *
+ * Every step's rows have c_eff entries, so all steps share one row_ptr:
+ *   row_ptr [T+1]               out: row_ptr[t] = t * c_eff.
+ *   col_idx [n_steps * nnz]     out: step step0+i's col_idx at offset i*nnz,
+ *                                    nnz = T * min(C, T).
+ *   info    [n_steps]           out, may be NULL: lvsa_mask_info of each step.
+ * The step-i mask is (row_ptr, col_idx + i*nnz, nnz) for lvsa_attention.
+ * Arguments otherwise as lvsa_build_mask; n_steps >= 1 and
+ * step0 + n_steps - 1 <= INT32_MAX.  Errors: LVSA_ERR_ARG, LVSA_ERR_CAPACITY
+ * (cap < n_steps * nnz); on error nothing is written. */
+int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps,
+                          int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                          lvsa_mask_info *info);
+
 /* Host check of a CSR frame mask (any source): row_ptr[0] == 0,
  * non-decreasing, row_ptr[T] == nnz, every row non-empty, ascending, unique
  * and within [0, T).  Errors: LVSA_ERR_ARG (null/negative sizes),

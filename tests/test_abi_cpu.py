@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     lib = L.library()
     names = header_functions()
     assert set(names) == {"lvsa_version", "lvsa_last_error", "lvsa_mask_nnz", "lvsa_build_mask",
-                          "lvsa_validate_mask", "lvsa_attention"}
+                          "lvsa_build_mask_steps", "lvsa_validate_mask", "lvsa_attention"}
     for n in names:
         assert hasattr(lib, n), n
     assert L.lvsa_version() == 1
@@ -69,6 +69,42 @@ def test_mask_bit_exact_sweep(flags):
                     rp, ci, _ = om.build_mask(T, C, W, s, flags)
                     assert m.col_idx.tolist() == ci, (T, C, W, s)
                     assert m.row_ptr.tolist() == rp
+
+
+@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T, L.LVSA_FIXED_GRID, L.LVSA_WINDOW_ONLY])
+def test_mask_steps_bit_exact(flags):
+    # A run of steps in one buffer: every step's block equals the oracle's
+    # mask of that step, and all steps share one row_ptr.
+    for T, C, W, step0, n in [(121, 21, 9, 0, 50), (49, 33, 13, 7, 13), (21, 21, 9, 0, 3), (8, 4, 2, 5, 11)]:
+        ms = L.lvsa_build_mask_steps(T, C, W, step0, n, flags)
+        assert tuple(ms.col_idx.shape) == (n, T * min(C, T))
+        for i in range(n):
+            rp, ci, info = om.build_mask(T, C, W, step0 + i, flags)
+            m = ms.mask(i)
+            assert m.row_ptr.tolist() == rp
+            assert m.col_idx.tolist() == ci, (T, C, W, step0 + i)
+            assert (m.c_eff, m.t_per, m.n_anchor, m.offset, m.nnz) == \
+                (info.c_eff, info.t_per, info.n_anchor, info.offset, info.nnz)
+
+
+def test_mask_steps_argument_errors():
+    lib = L.library()
+    rp = (ctypes.c_int32 * 200)()
+    ci = (ctypes.c_int32 * 4000)()
+    assert lib.lvsa_build_mask_steps(8, 4, 2, 0, 0, 0, rp, ci, 4000, None) == L.LVSA_ERR_ARG
+    assert lib.lvsa_build_mask_steps(8, 4, 2, -1, 3, 0, rp, ci, 4000, None) == L.LVSA_ERR_ARG
+    assert lib.lvsa_build_mask_steps(8, 4, 4, 0, 3, 0, rp, ci, 4000, None) == L.LVSA_ERR_ARG
+    assert lib.lvsa_build_mask_steps(8, 4, 2, 2**31 - 2, 3, 0, rp, ci, 4000, None) == L.LVSA_ERR_ARG
+    assert lib.lvsa_build_mask_steps(8, 4, 2, 0, 3, 0, None, ci, 4000, None) == L.LVSA_ERR_ARG
+    for i in range(100):
+        ci[i] = -7
+    # 3 steps of 32 entries need 96: one short is a capacity error, nothing written
+    assert lib.lvsa_build_mask_steps(8, 4, 2, 0, 3, 0, rp, ci, 95, None) == L.LVSA_ERR_CAPACITY
+    assert all(ci[i] == -7 for i in range(100))
+    assert lib.lvsa_build_mask_steps(8, 4, 2, 0, 3, 0, rp, ci, 96, None) == L.LVSA_OK
+    assert ci[96] == -7
+    with pytest.raises(IndexError):
+        L.lvsa_build_mask_steps(8, 4, 2, 0, 3).mask(3)
 
 
 def test_mask_nnz():
