@@ -336,7 +336,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-            "kernel": "lvsa_attn_fwd<128,4,1>", "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
+            "kernel": "lvsa_attn_fwd<128,4>", "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

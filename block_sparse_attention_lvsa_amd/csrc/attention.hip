@@ -76,9 +76,6 @@ typedef uint16_t u16;
 #ifndef LVSA_BN
 #define LVSA_BN 32
 #endif
-#ifndef LVSA_QB
-#define LVSA_QB 1
-#endif
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
@@ -141,11 +138,10 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 //        -> the transposing 8-byte reads that build the P·V operand (4
 //           consecutive keys × 4 quads of d per 16-lane group) are spread
 //           over distinct banks.
-template <int D, int NW, int QB>
+template <int D, int NW>
 struct Cfg {
   static constexpr int NT = NW * 64;          // threads per workgroup
-  static constexpr int QROWS = 32 * QB;       // query rows per wave (QB blocks of 32)
-  static constexpr int BM = NW * QROWS;       // query rows per workgroup
+  static constexpr int BM = NW * 32;          // query rows per workgroup (32 per wave)
   static constexpr int BN = LVSA_BN;          // keys per LDS tile
   static constexpr int KB = BN / 32;          // 32-key MFMA blocks per tile
   static constexpr int CH = D / 8;            // 16-byte chunks per key row
@@ -170,20 +166,18 @@ constexpr int kBufferFlags = 0x00020000;
 
 // One wave's state and steps.  Kept in a struct so that the per-tile step
 // can be specialised on the LDS buffer (immediate LDS offsets).  A wave owns
-// QB blocks of 32 query rows; every K and V operand read from LDS feeds QB
-// MFMAs.
-template <int D, int NW, int QB>
+// 32 query rows.
+template <int D, int NW>
 struct Block {
-  using C = Cfg<D, NW, QB>;
+  using C = Cfg<D, NW>;
 
   char *lds;
   int lane, wave, l32, hf;
   float scale_log2;
-  bool live[QB];               // block has at least one row inside the frame (wave-uniform)
-  bf16x8_t qf[QB][D / 16];     // Q rows, B-operand layout
-  f32x16_t oacc[QB][D / 32];   // Oᵀ accumulators (dims × 32 queries)
-  float m_run[QB];             // running row max, log2 domain (lazily raised)
-  float l_run[QB];             // this lane's partial row sum
+  bf16x8_t qf[D / 16];         // the wave's Q rows, B-operand layout
+  f32x16_t oacc[D / 32];       // Oᵀ accumulators (dims × 32 queries)
+  float m_run;                 // running row max, log2 domain (lazily raised)
+  float l_run;                 // this lane's partial row sum
   int32_t kro[D / 16];         // LDS byte offsets of this lane's K operands
   int32_t vro[D / 32];         // LDS byte offsets of this lane's V source rows
   int32_t koffb[C::LOADS_PER_WAVE], voffb[C::LOADS_PER_WAVE];  // load byte offsets
@@ -234,29 +228,25 @@ struct Block {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
   }
 
-  // Sᵀ (keys × 32 queries per block) of the K tile in buffer KBUF.
+  // Sᵀ (keys × 32 queries) of the K tile in buffer KBUF.
   template <int KBUF>
-  __device__ __forceinline__ void qk(f32x16_t (&sc)[QB][C::KB]) const {
+  __device__ __forceinline__ void qk(f32x16_t (&sc)[C::KB]) const {
     const char *Kb = lds + kTileOffK(KBUF);
 #pragma unroll
-    for (int q = 0; q < QB; ++q)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) sc[q][kb] = f32x16_t{};
+    for (int kb = 0; kb < C::KB; ++kb) sc[kb] = f32x16_t{};
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kb * 32 * C::ROWB);
-#pragma unroll
-        for (int q = 0; q < QB; ++q)
-          if (live[q]) sc[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[q][dc], sc[q][kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], sc[kb], 0, 0, 0);
       }
   }
 
   // Masks the keys >= kv of a run's tail tile, folds the tile's row maximum
   // into m_run (raised lazily, only when it would exceed it by more than
   // 2^kMaxLag) and rescales O and the row sum when it moves.
-  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv, int q) {
+  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv) {
     if (kv < C::BN) {
       // Empty asm: keeps this wave-uniform branch a branch (no speculation
       // of the selects into every tile).
@@ -278,15 +268,15 @@ struct Block {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
     mx = swap_halves_max(mx);
     const float mt = mx * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run[q] + kMaxLag) != 0) {
-      const float m_new = fmaxf(m_run[q], mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[q] - m_new);
-      l_run[q] *= alpha;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kMaxLag) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[q][i][e] *= alpha;
-      m_run[q] = m_new;
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+      m_run = m_new;
     }
   }
 
@@ -294,8 +284,8 @@ struct Block {
   // P = 2^(S·scale·log2e − m_run) rounded to bf16, in the MFMA B-operand
   // order of the P·V product; the row sum takes the same rounded values, so
   // the normalised weights sum to one.
-  __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB], int q) {
-    const float neg_m = -m_run[q];
+  __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB]) {
+    const float neg_m = -m_run;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -307,15 +297,14 @@ struct Block {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2_t pr = {pb[kb * 2 + m][e], pb[kb * 2 + m][e + 1]};
-          l_run[q] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[q], false);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
         }
       }
   }
 
-  // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF, for the query blocks in
-  // [q0, q1).
+  // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF.
   template <int VBUF>
-  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[QB][2 * C::KB], int q0, int q1) {
+  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[2 * C::KB]) {
     const char *Vb = lds + kTileOffV(VBUF);
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -327,38 +316,30 @@ struct Block {
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[dc] + krow + 8 * C::ROWB));
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int q = 0; q < QB; ++q)
-            if (q >= q0 && q < q1 && live[q])
-              oacc[q][dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[q][kb * 2 + m], oacc[q][dc], 0, 0, 0);
+          oacc[dc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kb * 2 + m], oacc[dc], 0, 0, 0);
         }
       }
   }
 
-  // One key tile from LDS buffer BUF.  With two query blocks the softmax of
-  // the second block runs while the P·V MFMAs of the first are in flight.
+  // One key tile from LDS buffer BUF.
   template <int BUF>
   __device__ __forceinline__ void tile(int kv) {
-    f32x16_t sc[QB][C::KB];
-    bf16x8_t pb[QB][2 * C::KB];
+    f32x16_t sc[C::KB];
+    bf16x8_t pb[2 * C::KB];
     qk<BUF>(sc);
-#pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      if (!live[q]) continue;
-      fold_max(sc[q], kv, q);
-      probs(sc[q], pb[q], q);
-      pv<BUF>(pb, q, q + 1);
-    }
+    fold_max(sc, kv);
+    probs(sc, pb);
+    pv<BUF>(pb);
   }
 };
 
-template <int D, int NW, int QB>
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
 void lvsa_attn_fwd(Args a) {
-  using C = Cfg<D, NW, QB>;
+  using C = Cfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];  // K0 V0 K1 V1
 
-  Block<D, NW, QB> blk;
+  Block<D, NW> blk;
   blk.lds = lds;
   const int tid = threadIdx.x;
   blk.lane = tid & 63;
@@ -386,14 +367,10 @@ void lvsa_attn_fwd(Args a) {
   const u16 *kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
   const u16 *vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
 
-  // ---- Q fragments: QB blocks of 32 rows × D per wave, B-operand layout
-  const int row0 = qt * C::BM + blk.wave * C::QROWS;  // first row of this wave within frame t
-  bool any_live = false;
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    blk.live[q] = row0 + q * 32 < P;  // wave-uniform
-    any_live |= blk.live[q];
-    const int r = row0 + q * 32 + blk.l32;
+  // ---- Q fragments: the wave's 32 rows × D, B-operand layout
+  const int row0 = qt * C::BM + blk.wave * 32;  // first row of this wave within frame t
+  {
+    const int r = row0 + blk.l32;
     const bool ok = r < P;
     const u16 *qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + ((int64_t)t * P + (ok ? r : 0)) * a.q_sn +
                     blk.hf * 8;
@@ -401,17 +378,18 @@ void lvsa_attn_fwd(Args a) {
     for (int dc = 0; dc < D / 16; ++dc) {
       bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(qp + dc * 16);
       if (!ok) x = bf16x8_t{};
-      blk.qf[q][dc] = x;
+      blk.qf[dc] = x;
     }
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) blk.oacc[q][i] = f32x16_t{};
-    blk.m_run[q] = -INFINITY;
-    blk.l_run[q] = 0.f;
   }
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) blk.oacc[i] = f32x16_t{};
+  blk.m_run = -INFINITY;
+  blk.l_run = 0.f;
   blk.init_offsets(a.k_sn, a.v_sn);
-  // Scalar copy of the wave-uniform flag, so the per-tile test is a scalar
-  // branch rather than a vector compare.
-  const int compute = __builtin_amdgcn_readfirstlane(any_live ? 1 : 0);
+  // Whether the wave has rows inside the frame (the last query tile of a
+  // frame may not fill every wave), as a scalar, so the per-tile test is a
+  // scalar branch rather than a vector compare.
+  const int compute = __builtin_amdgcn_readfirstlane(row0 < P ? 1 : 0);
 
   // ---- CSR row -> runs of key frames
   RunIter it;
@@ -477,23 +455,23 @@ void lvsa_attn_fwd(Args a) {
   if ((n_tiles & 1) && compute) blk.template tile<0>(kv);
 
   // ---- epilogue: normalise, round to bf16, store
-#pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int r = row0 + q * 32 + blk.l32;
+  {
+    const int r = row0 + blk.l32;
     // both lane halves hold the same row: reduce before the early exit
-    const float l_tot = swap_halves_sum(blk.l_run[q]);
-    if (r >= P) continue;
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + r) * a.o_sn;
+    const float l_tot = swap_halves_sum(blk.l_run);
+    if (r < P) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + r) * a.o_sn;
 #pragma unroll
-    for (int dc = 0; dc < D / 32; ++dc)
+      for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x4_t o4;
+        for (int i = 0; i < 4; ++i) {
+          bf16x4_t o4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(blk.oacc[q][dc][i * 4 + j] * inv);
-        *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + blk.hf * 4) = o4;
-      }
+          for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(blk.oacc[dc][i * 4 + j] * inv);
+          *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + blk.hf * 4) = o4;
+        }
+    }
   }
 }
 
@@ -547,9 +525,9 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
   return a0 < b1 && b0 < a1;
 }
 
-template <int D, int NW, int QB>
+template <int D, int NW>
 int launch(const Args &args, hipStream_t stream) {
-  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW, QB>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return lvsa::ok();
@@ -586,8 +564,7 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   const int D = (int)q->D;
   const int P = (int)(q->N / T);
   constexpr int NW = LVSA_NW;
-  constexpr int QB = LVSA_QB;
-  const int BM = NW * 32 * QB;
+  const int BM = NW * 32;
   const int q_tiles = (P + BM - 1) / BM;
   const int64_t n_wg = (int64_t)q->B * q->H * T * q_tiles;
   if (n_wg > INT32_MAX) return lvsa::fail(LVSA_ERR_SHAPE, "grid of %lld workgroups too large", (long long)n_wg);
@@ -613,6 +590,6 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   a.scale_log2 = sc * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128) return launch<128, NW, QB>(a, s);
-  return launch<64, NW, QB>(a, s);
+  if (D == 128) return launch<128, NW>(a, s);
+  return launch<64, NW>(a, s);
 }
