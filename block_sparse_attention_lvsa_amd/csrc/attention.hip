@@ -65,8 +65,9 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-// Tuning knobs (compile-time): waves per workgroup and the register budget
-// expressed as resident waves per SIMD.
+// Tuning knobs (compile-time): waves per workgroup, the register budget
+// expressed as resident waves per SIMD, keys per tile, and how many K operand
+// reads run ahead of the Q·Kᵀ MFMA chain.
 #ifndef LVSA_NW
 #define LVSA_NW 4
 #endif
@@ -75,6 +76,9 @@ typedef uint16_t u16;
 #endif
 #ifndef LVSA_BN
 #define LVSA_BN 32
+#endif
+#ifndef LVSA_KAHEAD
+#define LVSA_KAHEAD 3
 #endif
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
@@ -241,6 +245,18 @@ struct Block {
         const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kb * 32 * C::ROWB);
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[dc], sc[kb], 0, 0, 0);
       }
+#if LVSA_KAHEAD
+    // Issue order: LVSA_KAHEAD operand reads ahead of the dependent MFMA
+    // chain, then one read per MFMA, so each MFMA finds its K operand
+    // already loaded (the compiler's own order waits on every second read).
+    __builtin_amdgcn_sched_group_barrier(0x100, LVSA_KAHEAD, 1);
+#pragma unroll
+    for (int i = 0; i < D / 16 * C::KB - LVSA_KAHEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LVSA_KAHEAD, 1);
+#endif
   }
 
   // Masks the keys >= kv of a run's tail tile, folds the tile's row maximum
