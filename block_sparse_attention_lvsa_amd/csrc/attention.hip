@@ -94,12 +94,17 @@ struct Args {
   float scale_log2;  // softmax scale × log2(e)
 };
 
+// Read-only kernel inputs read at wave-uniform addresses go through the
+// constant address space, so they become scalar loads served by the scalar
+// cache instead of vector loads that each wait for memory.
+typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+
 // Walks one CSR row and yields maximal runs of consecutive frames as token
 // ranges [ks, ke).  Every value is wave-uniform (scalar registers).  An entry
 // outside [0, T), or not above the last frame taken, is skipped, so a
 // malformed row never causes an out-of-range read and never repeats a frame.
 struct RunIter {
-  const int32_t *cols;
+  const_i32p cols;
   int32_t e, e_end, T, P;
   int32_t last;  // last frame taken (-1 before the first)
   int32_t ks, ke;
@@ -410,10 +415,11 @@ void lvsa_attn_fwd(Args a) {
   // ---- CSR row -> runs of key frames
   RunIter it;
   {
-    int32_t rb = a.row_ptr[t], re = a.row_ptr[t + 1];
+    const const_i32p rp = (const_i32p)a.row_ptr;
+    int32_t rb = rp[t], re = rp[t + 1];
     rb = rb < 0 ? 0 : (rb > a.nnz ? a.nnz : rb);
     re = re < rb ? rb : (re > a.nnz ? a.nnz : re);
-    it.cols = a.col_idx;
+    it.cols = (const_i32p)a.col_idx;
     it.e = rb;
     it.e_end = re;
     it.T = a.T;
