@@ -53,6 +53,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "lvsa_internal.h"
 
@@ -540,6 +541,33 @@ void extent(const lvsa_tensor *x, uintptr_t *lo, uintptr_t *hi) {
   *hi = *lo + (uintptr_t)last * 2;
 }
 
+// True if two distinct elements of x share an address.  Sorts the
+// dimensions of size > 1 by stride and requires each stride to step past
+// the whole extent of the smaller ones (the usual test for a strided layout
+// without self-overlap; D is the contiguous innermost dimension).
+bool self_overlapping(const lvsa_tensor *x) {
+  int64_t st[3], sz[3];
+  int n = 0;
+  const int64_t dims[3][2] = {{x->stride_b, x->B}, {x->stride_h, x->H}, {x->stride_n, x->N}};
+  for (const auto &d : dims)
+    if (d[1] > 1) {
+      st[n] = d[0];
+      sz[n] = d[1];
+      ++n;
+    }
+  for (int i = 1; i < n; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      std::swap(st[j], st[j - 1]);
+      std::swap(sz[j], sz[j - 1]);
+    }
+  int64_t extent = x->D;  // elements spanned by the dimensions placed so far
+  for (int i = 0; i < n; ++i) {
+    if (st[i] < extent) return true;
+    extent = st[i] * (sz[i] - 1) + extent;
+  }
+  return false;
+}
+
 bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
   uintptr_t a0, a1, b0, b1;
   extent(a, &a0, &a1);
@@ -570,6 +598,8 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
       return lvsa::fail(LVSA_ERR_SHAPE, "q/k/v/out shapes differ");
   if (overlaps(out, q) || overlaps(out, k) || overlaps(out, v))
     return lvsa::fail(LVSA_ERR_SHAPE, "out overlaps an input tensor");
+  if (self_overlapping(out))
+    return lvsa::fail(LVSA_ERR_SHAPE, "out has overlapping elements (its strides alias two (b, h, token) rows)");
   if (T < 1) return lvsa::fail(LVSA_ERR_ARG, "T=%d: need T >= 1", T);
   if (q->N % T) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld is not a multiple of T=%d", (long long)q->N, T);
   if (q->N > INT32_MAX / 2) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld too large", (long long)q->N);

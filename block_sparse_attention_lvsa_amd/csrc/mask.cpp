@@ -15,6 +15,7 @@
 // anchors: O(C) per row, O(T·C) per step, no allocation beyond two O(T)
 // scratch vectors.
 #include <algorithm>
+#include <new>
 #include <vector>
 
 #include "lvsa_internal.h"
@@ -46,9 +47,10 @@ extern "C" int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out) 
   return lvsa::ok();
 }
 
-extern "C" int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags,
-                               int32_t *row_ptr, int32_t *col_idx, int32_t cap,
-                               lvsa_mask_info *info) {
+namespace {
+
+int build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags, int32_t *row_ptr,
+               int32_t *col_idx, int32_t cap, lvsa_mask_info *info) {
   int rc = check_domain(T, C, W, step, flags);
   if (rc) return rc;
   if (!row_ptr || !col_idx) return lvsa::fail(LVSA_ERR_ARG, "row_ptr/col_idx is NULL");
@@ -121,9 +123,8 @@ extern "C" int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, in
   return lvsa::ok();
 }
 
-extern "C" int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps,
-                                     int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
-                                     lvsa_mask_info *info) {
+int build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps, int32_t flags,
+                     int32_t *row_ptr, int32_t *col_idx, int64_t cap, lvsa_mask_info *info) {
   if (n_steps < 1) return lvsa::fail(LVSA_ERR_ARG, "n_steps=%d: need n_steps >= 1", n_steps);
   int rc = check_domain(T, C, W, step0, flags);
   if (rc) return rc;
@@ -137,18 +138,37 @@ extern "C" int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t st
                       (long long)(nnz * n_steps));
   // Every step's row offsets are the same (t * c_eff), so the first call
   // writes row_ptr and the others only their own block of col_idx.
+  std::vector<int32_t> scratch_rp(T + 1);
   for (int32_t i = 0; i < n_steps; ++i) {
-    int32_t *rp = i == 0 ? row_ptr : nullptr;
-    std::vector<int32_t> scratch_rp;
-    if (!rp) {
-      scratch_rp.resize(T + 1);
-      rp = scratch_rp.data();
-    }
-    rc = lvsa_build_mask(T, C, W, step0 + i, flags, rp, col_idx + (int64_t)i * nnz, (int32_t)nnz,
-                         info ? info + i : nullptr);
+    rc = build_mask(T, C, W, step0 + i, flags, i == 0 ? row_ptr : scratch_rp.data(),
+                    col_idx + (int64_t)i * nnz, (int32_t)nnz, info ? info + i : nullptr);
     if (rc) return rc;
   }
   return lvsa::ok();
+}
+
+}  // namespace
+
+// The C entry points: no C++ exception crosses the boundary (host memory
+// exhaustion in the builders' scratch vectors becomes an error status).
+extern "C" int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags,
+                               int32_t *row_ptr, int32_t *col_idx, int32_t cap,
+                               lvsa_mask_info *info) {
+  try {
+    return build_mask(T, C, W, step, flags, row_ptr, col_idx, cap, info);
+  } catch (const std::bad_alloc &) {
+    return lvsa::fail(LVSA_ERR_ARG, "out of host memory building the mask (T=%d)", T);
+  }
+}
+
+extern "C" int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps,
+                                     int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
+                                     lvsa_mask_info *info) {
+  try {
+    return build_mask_steps(T, C, W, step0, n_steps, flags, row_ptr, col_idx, cap, info);
+  } catch (const std::bad_alloc &) {
+    return lvsa::fail(LVSA_ERR_ARG, "out of host memory building the masks (T=%d)", T);
+  }
 }
 
 extern "C" int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx,

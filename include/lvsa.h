@@ -118,8 +118,9 @@ int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out);
  *   row_ptr [T+1] out: row_ptr[t] = t * c_eff.
  *   col_idx [cap] out: rows concatenated, each ascending and unique.
  *   info    out, may be NULL.
- * Errors: LVSA_ERR_ARG (domain, null row_ptr/col_idx), LVSA_ERR_CAPACITY
- *   (cap < T * min(C,T)); on error nothing is written. */
+ * Errors: LVSA_ERR_ARG (domain, null row_ptr/col_idx, host memory exhausted
+ *   for the builder's O(T) scratch), LVSA_ERR_CAPACITY (cap < T * min(C,T));
+ *   on error nothing is written. */
 int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags,
                     int32_t *row_ptr, int32_t *col_idx, int32_t cap,
                     lvsa_mask_info *info);
@@ -140,7 +141,8 @@ int lvsa_build_mask(int32_t T, int32_t C, int32_t W, int32_t step, int32_t flags
  * The step-i mask is (row_ptr, col_idx + i*nnz, nnz) for lvsa_attention.
  * Arguments otherwise as lvsa_build_mask; n_steps >= 1 and
  * step0 + n_steps - 1 <= INT32_MAX.  Errors: LVSA_ERR_ARG, LVSA_ERR_CAPACITY
- * (cap < n_steps * nnz); on error nothing is written. */
+ * (cap < n_steps * nnz); on an argument or capacity error nothing is written
+ * (if host memory runs out part way, earlier steps may have been). */
 int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_t n_steps,
                           int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
                           lvsa_mask_info *info);
@@ -166,7 +168,10 @@ int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx
  *
  * Arguments:
  *   q, k, v, out : [B, H, N, D] bf16 device tensors, identical B/H/N/D,
- *                  D in {64, 128}, N = T * P; out must not overlap q/k/v.
+ *                  D in {64, 128}, N = T * P.  out must not overlap q/k/v
+ *                  (byte extents) and no two of its (b, h, token) rows may
+ *                  share memory; q/k/v may (a stride of 0 broadcasts, e.g.
+ *                  one K/V head shared by several query heads).
  *   row_ptr_dev  : [T+1] int32 device array, CSR row offsets into col_idx.
  *   col_idx_dev  : [nnz] int32 device array, key frames of each query frame,
  *                  ascending and unique per row (lvsa_build_mask's output

@@ -183,6 +183,35 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
     assert "overlap" in (_attn(q, k, v, _rec(base + sz // 2)) and L.lvsa_last_error())
 
 
+def test_attention_rejects_self_overlapping_output():
+    base = 1 << 32
+    sz = 2 * 512 * 64 * 2
+    q, k, v = (_rec(base + i * sz) for i in range(3))
+    o = base + 3 * sz
+    for bad in (_rec(o, sh=0),                  # two heads on the same rows
+                _rec(o, sn=64, sh=64 * 256),    # heads 256 rows apart, 512 rows each
+                _rec(o, B=2, H=1, sb=0, sh=0)):  # two batch entries on the same rows
+        k2 = _rec(base + sz, B=bad.B, H=bad.H)
+        v2 = _rec(base + 2 * sz, B=bad.B, H=bad.H)
+        q2 = _rec(base, B=bad.B, H=bad.H)
+        assert _attn(q2, k2, v2, bad) == L.LVSA_ERR_SHAPE
+        assert "overlapping" in L.lvsa_last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers: the call must not reach a GPU")
+def test_attention_accepts_interleaved_heads_and_broadcast_inputs():
+    # [B, N, H, D] storage (heads interleaved within a token row) is not
+    # self-overlapping, and q/k/v may broadcast a head with stride 0: all
+    # argument checks pass and only the missing device is reported.
+    base = 1 << 32
+    sz = 2 * 512 * 64 * 2
+    q = _rec(base, sn=2 * 64, sh=64)
+    k = _rec(base + sz, sh=0)
+    v = _rec(base + 2 * sz, sh=0)
+    o = _rec(base + 3 * sz, sn=2 * 64, sh=64)
+    assert _attn(q, k, v, o) == L.LVSA_ERR_HIP
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_attention_without_device_reports_hip_error():
     base = 1 << 32

@@ -122,6 +122,21 @@ def test_strided_inputs_and_explicit_scale(gpu):
     assert_close(o, ref, "strided scale=0.05")
 
 
+def test_shared_kv_heads_by_zero_stride(gpu):
+    # Four query heads reading one K/V head through a head stride of 0 (the
+    # C ABI takes element strides): the result is that of the expanded K/V.
+    B, H, T, P, d, C, W = 1, 4, 9, 150, 128, 4, 2
+    say("shared K/V head", (B, H, T, P, d, C, W))
+    q = make_random((B, H, T * P, d), 351)
+    k1 = make_random((B, 1, T * P, d), 352)
+    v1 = make_random((B, 1, T * P, d), 353)
+    kd, vd = k1.to(gpu).expand(B, H, T * P, d), v1.to(gpu).expand(B, H, T * P, d)
+    assert kd.stride(1) == 0
+    o, rows = run_lib(q.to(gpu), kd, vd, T, C, W, 5)
+    ref = oa.block_attention(q, k1.expand(B, H, T * P, d).contiguous(), v1.expand(B, H, T * P, d).contiguous(), rows)
+    assert_close(o, ref, "shared K/V head (stride 0)")
+
+
 def test_custom_csr_masks(gpu):
     # Variable-length, non-LVSA rows (window-only / anchor-only ablations use
     # the same kernel): the kernel follows any ascending CSR row.
