@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Bar (north star of this path): masks bit-exact; attention max |Δ| ≤ 1e-2 and
+Bar: masks bit-exact; attention max |Δ| ≤ 1e-2 and
 mean |Δ| ≤ 1e-3 against the float64 oracle on the same bf16 inputs.  The
 tests also report (and bound) the relative RMS error, and use closed-form
 probes that read the mask back out of the kernel, because the absolute bar
