@@ -16,7 +16,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same step
   also          per-call kernel median/p10/p90, host mask build and mask H2D
                 times, dense comparator (same kernel, C = T mask) and speedup,
-                peak device memory; the same steps with every mask built
+                peak device memory; an outside reference (torch SDPA, flash
+                backend, dense, same tensors); the same steps with every mask built
                 ahead of time (one launch per step, and one HIP-graph replay
                 of the whole sequence); for workloads at the training horizon
                 (T <= C) the full-step / dense-kernel time ratios.
@@ -98,8 +99,31 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{w.name}: head 0, step 0, query frames 0..{done - 1} ({done} of {w.T} frames × {w.H} heads), "
-                  f"float64 torch-CPU, {dt:.1f} s",
+                  f"float64 torch-CPU, {dt:.1f} s, {threads} threads of {os.cpu_count()} host CPUs",
     }
+
+
+def sdpa_flash_dense_ms(q, k, v, reps=2):
+    """Outside reference, not on the LVSA path: torch's scaled_dot_product_attention
+    on the same tensors, dense (no mask), restricted to its flash backend (an
+    error instead of a fallback to the score-materialising math path).
+    Returns (ms per call, None) or (None, reason)."""
+    import torch
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            e1.record()
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, None
+    except Exception as ex:  # backend unavailable for this build or shape
+        return None, f"{type(ex).__name__}: {str(ex)[:160]}"
 
 
 def pct(xs, p):
@@ -253,6 +277,14 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
         res["dense_ms_per_call"] = dense_ms
         res["speedup_vs_dense_kernel"] = dense_ms / k_avg
         res["ideal_speedup_T_over_C"] = T / min(C, T)
+        # Outside reference (labelled as such): torch SDPA, flash backend, dense.
+        sdpa_ms, why = sdpa_flash_dense_ms(q, k, v)
+        res["outside_reference_torch_sdpa_flash_dense_ms"] = sdpa_ms
+        if sdpa_ms is None:
+            res["outside_reference_unavailable"] = why
+        else:
+            res["speedup_vs_torch_sdpa_flash_dense"] = sdpa_ms / k_avg
+        torch.cuda.empty_cache()
         if T <= C:
             # At the training horizon the method is the dense model: the full
             # step (host mask + H2D + kernel) against the dense kernel alone.
@@ -291,9 +323,10 @@ def main():
 
     if args.sweep:
         lines = ["| workload | B·H, T×P, C/W | ms/call (median) | effective TFLOP/s | % of 2.5 PF | dense (C=T) ms | "
-                 "speedup | ideal T/C | ms/step: host mask each step / prebuilt / graph | "
+                 "speedup | ideal T/C | torch SDPA flash, dense ms (outside reference) | "
+                 "ms/step: host mask each step / prebuilt / graph | "
                  "full step / dense (T≤C): host mask / graph | peak mem GB |",
-                 "|---|---|---|---|---|---|---|---|---|---|---|"]
+                 "|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for name in SWEEP:
             w = WORKLOADS[name]
             r = run_workload(w, args.steps, args.warmup, dense=True)
@@ -304,7 +337,9 @@ def main():
             lines.append(f"| {name} | {w.B * w.H}, {w.T}×{w.P}, {w.C}/{w.W} | {r['kernel_ms']['median']:.3f} | "
                          f"{r['kernel_tflops']:.1f} | {100 * r['kernel_tflops'] / PEAK_BF16_TFLOPS:.1f} | "
                          f"{r['dense_ms_per_call']:.3f} | {r['speedup_vs_dense_kernel']:.2f} | "
-                         f"{r['ideal_speedup_T_over_C']:.2f} | {sm['host_mask_each_step']:.3f} / "
+                         f"{r['ideal_speedup_T_over_C']:.2f} | "
+                         f"{'%.1f' % r['outside_reference_torch_sdpa_flash_dense_ms'] if r.get('outside_reference_torch_sdpa_flash_dense_ms') else 'n/a'} | "
+                         f"{sm['host_mask_each_step']:.3f} / "
                          f"{sm['prebuilt_masks']:.3f} / {sm['graph_replay']:.3f} | "
                          f"{'%.3f / %.3f' % (ov, og) if ov else '—'} | {r['max_memory_allocated_gb']:.1f} |")
             torch.cuda.empty_cache()
@@ -331,6 +366,10 @@ def main():
     if "dense_ms_per_call" in r:
         log(f"dense (C=T) kernel: {r['dense_ms_per_call']:.3f} ms -> speedup {r['speedup_vs_dense_kernel']:.2f}x "
             f"(ideal {r['ideal_speedup_T_over_C']:.2f}x)")
+        if r.get("outside_reference_torch_sdpa_flash_dense_ms"):
+            log(f"outside reference, torch SDPA (flash backend, dense): "
+                f"{r['outside_reference_torch_sdpa_flash_dense_ms']:.2f} ms -> LVSA kernel "
+                f"{r['speedup_vs_torch_sdpa_flash_dense']:.2f}x faster")
 
     achieved = r["kernel_tflops"]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -346,7 +385,9 @@ def main():
 
     extra = {key: (round(val, 4) if isinstance(val, float) else val) for key, val in r.items()
              if key in ("dense_ms_per_call", "speedup_vs_dense_kernel", "ideal_speedup_T_over_C",
-                        "full_step_over_dense_kernel", "graph_step_over_dense_kernel", "mask_build_us_median",
+                        "full_step_over_dense_kernel", "graph_step_over_dense_kernel",
+                        "outside_reference_torch_sdpa_flash_dense_ms", "speedup_vs_torch_sdpa_flash_dense",
+                        "outside_reference_unavailable", "mask_build_us_median",
                         "mask_h2d_ms_median", "max_memory_allocated_gb")}
     if "step_modes_ms" in r:
         extra["step_modes_ms"] = {key: round(val, 4) for key, val in r["step_modes_ms"].items()}
