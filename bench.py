@@ -2,7 +2,10 @@
 
 One step = one denoising step of the attention hot path over the whole
 workload: build the step's CSR mask on the host (C++), copy it to the device,
-run the frame-block-sparse attention kernel on [B, H, T·P, d] bf16.  The
+run the frame-block-sparse attention on [B, H, T·P, d] bf16 (by default
+through lvsa_attention_ws: a key-norm pass, then the attention kernel with a
+fixed softmax reference where the norm bound allows; --no-workspace times
+lvsa_attention, the running-max path).  The
 default workload is the Wan-2.1-1.3B-shaped 6× horizon: B=1, H=12, d=128,
 T=121 latent frames × 1560 tokens (480×832 video), C=21, W=9, anchors
 rotating with the step (seeded synthetic N(0,1) inputs, resident in HBM before
@@ -131,7 +134,7 @@ def pct(xs, p):
     return xs[min(len(xs) - 1, int(p * len(xs)))]
 
 
-def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, modes=True):
+def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, modes=True, workspace=True):
     """Times `steps` full hot-path steps of workload `w`; returns a dict."""
     import torch
     import block_sparse_attention_lvsa_amd as L
@@ -166,6 +169,19 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
     d_ci = torch.empty(nnz, dtype=torch.int32, device=dev)
     info = L.LvsaMaskInfo()
     recs = [L._tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    # With a workspace the call is lvsa_attention_ws: a key-norm pass, then
+    # the attention with a fixed softmax reference where the bound allows.
+    ws_bytes = L.lvsa_attention_workspace_bytes(w.B, w.H, T) if workspace else 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def attention(rp_ptr, ci_ptr, sptr):
+        if workspace:
+            return lib.lvsa_attention_ws(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
+                                         ctypes.c_void_p(rp_ptr), ctypes.c_void_p(ci_ptr), T, nnz,
+                                         ctypes.byref(recs[3]), 0.0, ctypes.c_void_p(ws.data_ptr()), ws_bytes, sptr)
+        return lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
+                                  ctypes.c_void_p(rp_ptr), ctypes.c_void_p(ci_ptr), T, nnz,
+                                  ctypes.byref(recs[3]), 0.0, sptr)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -185,9 +201,7 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
         d_ci.copy_(h_ci[i], non_blocking=True)
         if ev is not None:
             ev[1].record(stream)
-        rc = lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
-                                ctypes.c_void_p(d_rp.data_ptr()), ctypes.c_void_p(d_ci.data_ptr()),
-                                T, nnz, ctypes.byref(recs[3]), 0.0, sp)
+        rc = attention(d_rp.data_ptr(), d_ci.data_ptr(), sp)
         if ev is not None:
             ev[2].record(stream)
         if rc:
@@ -223,6 +237,8 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
         "mask_build_us_median": statistics.median(mask_times) * 1e6,
         "mask_h2d_ms_median": statistics.median(h2d),
         "flops_per_step": flops,
+        "path": "lvsa_attention_ws (key-norm pass + fixed softmax reference where the bound allows)" if workspace
+                else "lvsa_attention (running-max softmax)",
     }
     if modes:
         # The same steps with no per-step host work: all masks built ahead of
@@ -234,10 +250,7 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
         def launch_all():
             sptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
             for j in range(steps):
-                rc = lib.lvsa_attention(ctypes.byref(recs[0]), ctypes.byref(recs[1]), ctypes.byref(recs[2]),
-                                        ctypes.c_void_p(ms.row_ptr.data_ptr()),
-                                        ctypes.c_void_p(ms.col_idx[j].data_ptr()),
-                                        T, nnz, ctypes.byref(recs[3]), 0.0, sptr)
+                rc = attention(ms.row_ptr.data_ptr(), ms.col_idx[j].data_ptr(), sptr)
                 if rc:
                     raise RuntimeError(L.lvsa_last_error())
 
@@ -263,14 +276,15 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
     if dense:
         # Dense comparator: the same kernel with a C = T mask (one run of N keys).
         dm = L.lvsa_build_mask(T, max(T, 2), 1, 0).to(dev)
-        L.lvsa_attention(q, k, v, dm, out=out)
+        dws = ws if workspace else None
+        L.lvsa_attention(q, k, v, dm, out=out, workspace=dws)
         torch.cuda.synchronize()
         reps = 3
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
-            L.lvsa_attention(q, k, v, dm, out=out)
+            L.lvsa_attention(q, k, v, dm, out=out, workspace=dws)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / reps
@@ -306,6 +320,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="time lvsa_attention (running-max softmax) instead of lvsa_attention_ws")
     ap.add_argument("--no-step-modes", action="store_true",
                     help="skip the prebuilt-mask and graph-replay timings of the same steps")
     ap.add_argument("--calib-copy", action="store_true",
@@ -329,7 +345,7 @@ def main():
                  "|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for name in SWEEP:
             w = WORKLOADS[name]
-            r = run_workload(w, args.steps, args.warmup, dense=True)
+            r = run_workload(w, args.steps, args.warmup, dense=True, workspace=not args.no_workspace)
             log(json.dumps(r))
             ov = r.get("full_step_over_dense_kernel")
             og = r.get("graph_step_over_dense_kernel")
@@ -353,7 +369,8 @@ def main():
     w = WORKLOADS[args.workload]
     log(f"workload {w}")
     r = run_workload(w, args.steps, args.warmup, dense=not args.no_dense, calib_copy=args.calib_copy,
-                     keep_inputs=not args.no_cpu_baseline, modes=not args.no_step_modes)
+                     keep_inputs=not args.no_cpu_baseline, modes=not args.no_step_modes,
+                     workspace=not args.no_workspace)
     log(f"step: {r['ms_per_step']:.3f} ms  kernel avg {r['kernel_ms']['avg']:.3f} ms (median "
         f"{r['kernel_ms']['median']:.3f}, p10 {r['kernel_ms']['p10']:.3f}, p90 {r['kernel_ms']['p90']:.3f})  "
         f"{r['value']:.1f} TFLOP/s effective, kernel {r['kernel_tflops']:.1f} TFLOP/s")
@@ -375,7 +392,9 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-            "kernel": "lvsa_attn_fwd<128,4>", "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
+            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_key_norms<128> in the timed call)"
+                                                if not args.no_workspace else ""),
+            "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -388,7 +407,7 @@ def main():
                         "full_step_over_dense_kernel", "graph_step_over_dense_kernel",
                         "outside_reference_torch_sdpa_flash_dense_ms", "speedup_vs_torch_sdpa_flash_dense",
                         "outside_reference_unavailable", "mask_build_us_median",
-                        "mask_h2d_ms_median", "max_memory_allocated_gb")}
+                        "mask_h2d_ms_median", "max_memory_allocated_gb", "path")}
     if "step_modes_ms" in r:
         extra["step_modes_ms"] = {key: round(val, 4) for key, val in r["step_modes_ms"].items()}
     extra["kernel_ms"] = {key: round(val, 4) for key, val in r["kernel_ms"].items()}

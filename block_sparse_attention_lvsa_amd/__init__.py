@@ -16,7 +16,9 @@ Functions with the ABI's names:
   lvsa_build_mask(T, C, W, step, flags=LVSA_ROT_MOD_TPER) -> Mask (host int32)
   lvsa_build_mask_steps(T, C, W, step0, n_steps, flags=...) -> MaskSteps (host int32)
   lvsa_validate_mask(T, row_ptr, col_idx)
-  lvsa_attention(q, k, v, mask_dev, out=None, scale=None, stream=None) -> out
+  lvsa_attention(q, k, v, mask_dev, out=None, scale=None, stream=None, workspace=None) -> out
+      (with a workspace: the C ABI's lvsa_attention_ws)
+  lvsa_attention_workspace_bytes(B, H, T) -> int
 
 ``Mask.to(device)`` copies the CSR arrays (``non_blocking`` on the current
 stream) for ``lvsa_attention``.  ``MaskSteps`` holds the masks of a run of
@@ -104,6 +106,13 @@ def library() -> ctypes.CDLL:
         lib.lvsa_attention.argtypes = [ctypes.POINTER(LvsaTensor)] * 3 + [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.POINTER(LvsaTensor), ctypes.c_float, ctypes.c_void_p]
+        lib.lvsa_attention_ws.restype = ctypes.c_int
+        lib.lvsa_attention_ws.argtypes = [ctypes.POINTER(LvsaTensor)] * 3 + [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.POINTER(LvsaTensor), ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.lvsa_attention_workspace_bytes.restype = ctypes.c_int
+        lib.lvsa_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                       ctypes.POINTER(ctypes.c_int64)]
         _LIB = lib
     return _LIB
 
@@ -233,11 +242,20 @@ def _tensor_record(x, name: str) -> LvsaTensor:
                       LVSA_DTYPE_BF16 if x.dtype == torch.bfloat16 else 0)
 
 
-def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None, stream=None):
+def lvsa_attention_workspace_bytes(B: int, H: int, T: int) -> int:
+    """Device workspace bytes lvsa_attention needs when given a workspace."""
+    n = ctypes.c_int64(0)
+    _check(library().lvsa_attention_workspace_bytes(B, H, T, ctypes.byref(n)))
+    return n.value
+
+
+def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None, stream=None, workspace=None):
     """Frame-block-sparse attention on the GPU (see include/lvsa.h).
 
     q, k, v, out: [B, H, T·P, D] bf16 CUDA tensors; mask: a Mask whose
-    arrays are already on q's device.  Launches on ``stream`` (default: the
+    arrays are already on q's device.  ``workspace``: optional device tensor
+    of at least lvsa_attention_workspace_bytes(B, H, T) bytes (then the call
+    is the ABI's lvsa_attention_ws).  Launches on ``stream`` (default: the
     current stream) and returns ``out`` without synchronising.
     """
     import torch
@@ -252,9 +270,15 @@ def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(library().lvsa_attention(ctypes.byref(rq), ctypes.byref(rk), ctypes.byref(rv),
-                                    ctypes.c_void_p(mask.row_ptr.data_ptr()),
-                                    ctypes.c_void_p(mask.col_idx.data_ptr()),
-                                    mask.T, mask.col_idx.numel(), ctypes.byref(ro),
-                                    0.0 if scale is None else float(scale), ctypes.c_void_p(sp)))
+    args = (ctypes.byref(rq), ctypes.byref(rk), ctypes.byref(rv),
+            ctypes.c_void_p(mask.row_ptr.data_ptr()), ctypes.c_void_p(mask.col_idx.data_ptr()),
+            mask.T, mask.col_idx.numel(), ctypes.byref(ro), 0.0 if scale is None else float(scale))
+    if workspace is None:
+        _check(library().lvsa_attention(*args, ctypes.c_void_p(sp)))
+    else:
+        if not workspace.is_cuda or workspace.device != q.device:
+            raise LvsaValueError(LVSA_ERR_ARG, f"workspace: need a device tensor on {q.device}")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(library().lvsa_attention_ws(*args, ctypes.c_void_p(workspace.data_ptr()), nbytes,
+                                           ctypes.c_void_p(sp)))
     return out

@@ -84,6 +84,11 @@ typedef uint16_t u16;
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
+// Largest log2 gap a fixed softmax reference may leave below a row's true
+// maximum: with the reference at most 96 above it (its bound, below), the
+// largest probability of the row stays >= 2^-96, far inside the normal
+// range of fp32 and bf16 (2^-126).
+constexpr float kMaxRefGap = 96.0f;
 
 struct Args {
   const u16 *q, *k, *v;
@@ -93,12 +98,16 @@ struct Args {
   const int32_t *row_ptr, *col_idx;
   int32_t nnz, T, P, H, q_tiles, n_wg;
   float scale_log2;  // softmax scale × log2(e)
+  // Largest key norm of every (b, h, frame), [B·H·T], or null: then every
+  // wave uses the running-max softmax.
+  const float *kmax;
 };
 
 // Read-only kernel inputs read at wave-uniform addresses go through the
 // constant address space, so they become scalar loads served by the scalar
 // cache instead of vector loads that each wait for memory.
 typedef const __attribute__((address_space(4))) int32_t *const_i32p;
+typedef const __attribute__((address_space(4))) float *const_f32p;
 
 // Walks one CSR row and yields maximal runs of consecutive frames as token
 // ranges [ks, ke).  Every value is wave-uniform (scalar registers).  An entry
@@ -183,6 +192,7 @@ struct Block {
 
   char *lds;
   int lane, wave, l32, hf;
+  int fixed_ref;               // the wave's reference is a fixed bound (no running max), wave-uniform
   float scale_log2;
   bf16x8_t qf[D / 16];         // the wave's Q rows, B-operand layout
   f32x16_t oacc[D / 32];       // Oᵀ accumulators (dims × 32 queries)
@@ -283,6 +293,7 @@ struct Block {
           if ((e >> 2) * 8 + (e & 3) >= thr) sc[kb][e] = -INFINITY;
       }
     }
+    if (fixed_ref) return;  // m_run bounds every score of the row: nothing to fold
     float mx = sc[0][0];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -433,6 +444,37 @@ void lvsa_attn_fwd(Args a) {
   // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
   // barrier per tile.  Unrolled by two so that every LDS offset is an
   // immediate.
+  // ---- softmax reference.  Without a key-norm table: the running max,
+  // raised lazily.  With one: by Cauchy-Schwarz every score of query i is at
+  // most |q_i|·K, K the largest key norm over the row's frames, so
+  // m_i = scale·log2e·|q_i|·K·(1 + 2^-8) bounds every exponent by 0 (the
+  // factor covers the rounding of the fp32 norms and of the MFMA dot
+  // products) and no running max or rescale is needed.  A wave uses it only
+  // if no lane's bound is more than kMaxRefGap above that lane's true
+  // maximum (scores are >= -|q_i|·K, so 2·m_i <= kMaxRefGap suffices).
+  blk.fixed_ref = 0;
+  if (a.kmax) {
+    const const_f32p km = (const_f32p)(a.kmax + (int64_t)bh * a.T);
+    float kn = 0.f;
+    for (int32_t e = it.e; e < it.e_end; ++e) {
+      const int32_t f = it.cols[e];
+      if (f >= 0 && f < a.T) kn = fmaxf(kn, km[f]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)blk.qf[dc][e];
+        ss = __builtin_fmaf(x, x, ss);
+      }
+    ss = swap_halves_sum(ss);  // |q_i|^2: each lane half holds half of the row
+    const float m_ref = a.scale_log2 * __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
+    const bool use = __builtin_amdgcn_ballot_w64(!(2.0f * m_ref <= kMaxRefGap)) == 0;
+    if (use) blk.m_run = m_ref;
+    blk.fixed_ref = __builtin_amdgcn_readfirstlane(use ? 1 : 0);
+  }
+
   int n_tiles = 0;
   {
     RunIter c = it;
@@ -496,6 +538,39 @@ void lvsa_attn_fwd(Args a) {
         }
     }
   }
+}
+
+// Largest key norm of one (b, h, frame): one workgroup per frame streams its
+// P key rows once (16 bytes per lane, D/8 lanes per row) and writes
+// max_j |k_j| (fp32 sums of squares of the bf16 values) to kmax[(b·H + h)·T + t].
+template <int D>
+__global__ __launch_bounds__(256) void lvsa_key_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
+                                                      int32_t H, int32_t T, int32_t P, float *kmax) {
+  constexpr int LPR = D / 8;          // lanes per key row
+  constexpr int RPI = 256 / LPR;      // rows per workgroup iteration
+  const int item = blockIdx.x;        // (b·H + h)·T + t
+  const int t = item % T;
+  const int bh = item / T;
+  const int h = bh % H;
+  const int b = bh / H;
+  const u16 *base = k + (int64_t)b * k_sb + (int64_t)h * k_sh + (int64_t)t * P * k_sn;
+  const int col = (threadIdx.x % LPR) * 8;
+  float best = 0.f;
+  for (int r = threadIdx.x / LPR; r < P; r += RPI) {
+    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(base + (int64_t)r * k_sn + col);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf((float)x[e], (float)x[e], ss);
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);  // the row's LPR lanes
+    best = fmaxf(best, ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) kmax[item] = __builtin_sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 }
 
 // ------------------------------------------------------------------ host --
@@ -577,18 +652,27 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
 
 template <int D, int NW>
 int launch(const Args &args, hipStream_t stream) {
+  if (args.kmax) {
+    // the key-norm table first, on the same stream
+    hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
+                       args.k_sh, args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.kmax));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "key-norm kernel launch failed: %s", hipGetErrorString(e));
+  }
   hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return lvsa::ok();
 }
 
-}  // namespace
+int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t T) {
+  return ((B * H * T * (int64_t)sizeof(float) + 255) / 256) * 256;
+}
 
-extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
-                              const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
-                              int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
-                              void *stream) {
+int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                   const int32_t *row_ptr_dev, const int32_t *col_idx_dev, int32_t T, int32_t nnz,
+                   lvsa_tensor *out, float scale, void *workspace, int64_t workspace_bytes, bool use_ws,
+                   void *stream) {
   int rc;
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(out, "out")))
@@ -609,6 +693,20 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
     uint32_t bits;  // exponent all ones: inf or NaN (a bit test no fast-math flag can fold)
     std::memcpy(&bits, &scale, sizeof bits);
     if ((bits & 0x7f800000u) == 0x7f800000u) return lvsa::fail(LVSA_ERR_ARG, "scale is not finite");
+  }
+  if (use_ws) {
+    const int64_t need = workspace_bytes_for(q->B, q->H, T);
+    if (!workspace) return lvsa::fail(LVSA_ERR_ARG, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 4) return lvsa::fail(LVSA_ERR_ARG, "workspace not 4-byte aligned");
+    if (workspace_bytes < need)
+      return lvsa::fail(LVSA_ERR_CAPACITY, "workspace of %lld bytes < required %lld", (long long)workspace_bytes,
+                        (long long)need);
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(workspace), w1 = w0 + (uintptr_t)need;
+    for (const lvsa_tensor *x : {q, k, v, (const lvsa_tensor *)out}) {
+      uintptr_t x0, x1;
+      extent(x, &x0, &x1);
+      if (w0 < x1 && x0 < w1) return lvsa::fail(LVSA_ERR_ARG, "workspace overlaps a tensor");
+    }
   }
   int dev;
   if ((rc = check_device(&dev))) return rc;
@@ -640,8 +738,34 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   a.n_wg = (int32_t)n_wg;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.kmax = use_ws ? static_cast<const float *>(workspace) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) return launch<128, NW>(a, s);
   return launch<64, NW>(a, s);
+}
+
+}  // namespace
+
+extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                              const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                              int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
+                              void *stream) {
+  return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, nullptr, 0, false, stream);
+}
+
+extern "C" int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes) {
+  if (!bytes) return lvsa::fail(LVSA_ERR_ARG, "bytes is NULL");
+  if (B < 1 || H < 1 || T < 1) return lvsa::fail(LVSA_ERR_ARG, "B, H and T must be >= 1");
+  if (B * H > (int64_t{1} << 40) / T) return lvsa::fail(LVSA_ERR_ARG, "B*H*T too large");
+  *bytes = workspace_bytes_for(B, H, T);
+  return lvsa::ok();
+}
+
+extern "C" int lvsa_attention_ws(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                                 const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                                 int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
+                                 void *workspace, int64_t workspace_bytes, void *stream) {
+  return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, workspace, workspace_bytes, true,
+                        stream);
 }

@@ -13,9 +13,10 @@
  *   - Return value: LVSA_OK (0) or a negative LVSA_ERR_* code.  A readable
  *     message for the last failure on the calling thread is returned by
  *     lvsa_last_error().
- *   - Ownership: the caller owns every buffer, host and device.  The library
- *     allocates no device memory, frees nothing, keeps no pointer after the
- *     call returns, and never synchronises a stream.
+ *   - Ownership: the caller owns every buffer, host and device, including
+ *     the optional workspace of lvsa_attention_ws.  The library allocates no
+ *     device memory, frees nothing, keeps no pointer after the call returns,
+ *     and never synchronises a stream.
  *   - Thread safety: all calls are reentrant; error messages are per thread.
  */
 #ifndef LVSA_H_
@@ -192,6 +193,39 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
                    int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
                    void *stream);
+
+/* Bytes of device workspace lvsa_attention_ws needs for B, H and T: one
+ * float per (b, h, frame), rounded up to 256.  Errors: LVSA_ERR_ARG. */
+int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes);
+
+/* lvsa_attention with a caller-provided device workspace, used to drop the
+ * online softmax's running maximum where that is safe.
+ *
+ * Source: the same computation as lvsa_attention (gist.science explainer,
+ * Technical Summary §2).  The workspace changes only the softmax's reference
+ * point, which cancels in the normalisation: a first kernel writes the
+ * largest key norm of every (b, h, frame) to the workspace; then, by
+ * Cauchy-Schwarz, scale·|q_i|·(largest key norm over A(t)) bounds every
+ * score of query i, and a wave whose 64 lanes all have bounds close enough
+ * to their true maxima (within 2^96 in probability) uses that bound as a
+ * fixed reference -- no running maximum, no rescaling.  Other waves (large
+ * query/key norms) keep the running-maximum path.  Results agree with
+ * lvsa_attention to the same accuracy, not bit for bit (the probabilities
+ * are rounded to bf16 at a different scale).
+ *
+ * Arguments as lvsa_attention, plus:
+ *   workspace        : device memory of at least
+ *                      lvsa_attention_workspace_bytes(B, H, T) bytes,
+ *                      4-byte aligned, not overlapping q/k/v/out.  Owned by
+ *                      the caller; overwritten by the call (stream-ordered),
+ *                      so concurrent calls need separate workspaces.
+ *   workspace_bytes  : its size.
+ * Errors: those of lvsa_attention; LVSA_ERR_ARG (NULL, misaligned or
+ * overlapping workspace), LVSA_ERR_CAPACITY (too small). */
+int lvsa_attention_ws(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                      const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                      int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
+                      void *workspace, int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

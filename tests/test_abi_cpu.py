@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     lib = L.library()
     names = header_functions()
     assert set(names) == {"lvsa_version", "lvsa_last_error", "lvsa_mask_nnz", "lvsa_build_mask",
-                          "lvsa_build_mask_steps", "lvsa_validate_mask", "lvsa_attention"}
+                          "lvsa_build_mask_steps", "lvsa_validate_mask", "lvsa_attention",
+                          "lvsa_attention_ws", "lvsa_attention_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
     assert L.lvsa_version() == 1
@@ -181,6 +182,37 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
     assert _attn(q, k, v, o, scale=float("nan")) == L.LVSA_ERR_ARG
     assert _attn(_rec(0), k, v, o) == L.LVSA_ERR_ARG
     assert "overlap" in (_attn(q, k, v, _rec(base + sz // 2)) and L.lvsa_last_error())
+
+
+def test_workspace_bytes():
+    assert L.lvsa_attention_workspace_bytes(1, 12, 121) == 5888  # 1452 floats, rounded up to 256 bytes
+    assert L.lvsa_attention_workspace_bytes(1, 2, 8) == 256
+    assert L.lvsa_attention_workspace_bytes(2, 40, 121) == 38912
+    lib = L.library()
+    n = ctypes.c_int64(0)
+    assert lib.lvsa_attention_workspace_bytes(0, 2, 8, ctypes.byref(n)) == L.LVSA_ERR_ARG
+    assert lib.lvsa_attention_workspace_bytes(1, 2, 8, None) == L.LVSA_ERR_ARG
+
+
+def _attn_ws(q, k, v, o, ws, ws_bytes, T=8, nnz=32, rp=0x1000, ci=0x2000):
+    lib = L.library()
+    return lib.lvsa_attention_ws(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                 ctypes.c_void_p(rp), ctypes.c_void_p(ci), T, nnz,
+                                 ctypes.byref(o), 0.0, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_workspace_errors_are_reported_before_any_device_work():
+    base = 1 << 32
+    sz = 2 * 512 * 64 * 2
+    q, k, v, o = (_rec(base + i * sz) for i in range(4))
+    ws = base + 8 * sz
+    assert _attn_ws(q, k, v, o, 0, 256) == L.LVSA_ERR_ARG                 # NULL
+    assert "NULL" in L.lvsa_last_error()
+    assert _attn_ws(q, k, v, o, ws + 2, 256) == L.LVSA_ERR_ARG            # misaligned
+    assert _attn_ws(q, k, v, o, ws, 255) == L.LVSA_ERR_CAPACITY           # 2·8 floats -> 256 bytes
+    assert _attn_ws(q, k, v, o, base + 16, 256) == L.LVSA_ERR_ARG         # inside q
+    assert "overlaps" in L.lvsa_last_error()
+    assert _attn_ws(_rec(base, dtype=0), k, v, o, ws, 256) == L.LVSA_ERR_DTYPE  # the plain checks still apply
 
 
 def test_attention_rejects_self_overlapping_output():

@@ -265,6 +265,106 @@ def test_deterministic(gpu):
     assert torch.equal(a, b)
 
 
+# ------------------------ the workspace path (fixed softmax reference) --
+
+
+def workspace_for(q, T):
+    B, H = q.shape[0], q.shape[1]
+    return torch.empty(L.lvsa_attention_workspace_bytes(B, H, T), dtype=torch.uint8, device=q.device)
+
+
+@pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_FIXED_GRID, L.LVSA_WINDOW_ONLY])
+def test_workspace_tiny_all_steps(gpu, flags):
+    w = WORKLOADS["tiny"]
+    say("workspace tiny", w, "flags", flags)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    ws = workspace_for(qd, w.T)
+    for s in w.steps:
+        m = L.lvsa_build_mask(w.T, w.C, w.W, s, flags).to(gpu)
+        o = L.lvsa_attention(qd, kd, vd, m, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(o, oa.block_attention(q, k, v, om.key_frames(w.T, w.C, w.W, s, flags)), f"ws tiny step {s}")
+
+
+@pytest.mark.parametrize("case", MID_CASES, ids=lambda c: "B%dH%dT%dP%dd%dC%dW%d" % c[:7])
+def test_workspace_mid_size(gpu, case):
+    B, H, T, P, d, C, W, seed = case
+    say("workspace mid", case)
+    q = make_random((B, H, T * P, d), seed)
+    k = make_random((B, H, T * P, d), seed + 1000)
+    v = make_random((B, H, T * P, d), seed + 2000)
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    ws = workspace_for(qd, T)
+    for s in (0, 5):
+        m = L.lvsa_build_mask(T, C, W, s).to(gpu)
+        o = L.lvsa_attention(qd, kd, vd, m, workspace=ws)
+        o_exact = L.lvsa_attention(qd, kd, vd, m)
+        torch.cuda.synchronize()
+        assert_close(o, oa.block_attention(q, k, v, om.key_frames(T, C, W, s)), f"ws mid {case} step {s}")
+        assert_close(o, o_exact.double().cpu(), f"ws vs exact path, step {s}")
+
+
+def test_workspace_takes_the_fixed_reference_and_falls_back_on_large_norms(gpu):
+    # Unit-variance d=128 inputs: every wave's bound is close enough, so the
+    # fixed reference is used (outputs round differently from the running-max
+    # path).  Keys shifted by a large common vector make |q|·max|k| far above
+    # the true scores: every wave must fall back, giving the running-max
+    # path's output bit for bit.  Mixed: large-norm query rows in some waves.
+    T, P, d, C, W = 9, 200, 128, 4, 2
+    say("workspace reference choice", (T, P, d, C, W))
+    q = make_random((1, 2, T * P, d), 901)
+    k = make_random((1, 2, T * P, d), 902)
+    v = make_random((1, 2, T * P, d), 903)
+    m = L.lvsa_build_mask(T, C, W, 1).to(gpu)
+    rows = om.key_frames(T, C, W, 1)
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    ws = workspace_for(qd, T)
+    a = L.lvsa_attention(qd, kd, vd, m, workspace=ws)
+    b = L.lvsa_attention(qd, kd, vd, m)
+    torch.cuda.synchronize()
+    assert not torch.equal(a, b)  # the fixed reference was used
+    assert_close(a, oa.block_attention(q, k, v, rows), "fixed reference")
+    u = q.float().mean(dim=(0, 1, 2))
+    k_far = (k.float() + u / u.norm() * 400.0).to(torch.bfloat16)
+    a = L.lvsa_attention(qd, k_far.to(gpu), vd, m, workspace=ws)
+    b = L.lvsa_attention(qd, k_far.to(gpu), vd, m)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)  # every wave fell back to the running max
+    toks = [0, 77, 199, 200, 1234, T * P - 1]
+    assert_close(a[0, 0, toks], oa.block_attention_rows(q, k_far, v, rows, 0, 0, toks), "fallback")
+    q_mixed = q.clone()
+    q_mixed[:, :, 300:340] *= 60.0  # rows 300..339 of frame 1: two waves fall back, the others do not
+    qmd = q_mixed.to(gpu)
+    a = L.lvsa_attention(qmd, kd, vd, m, workspace=ws)
+    torch.cuda.synchronize()
+    toks = [0, 250, 299, 300, 320, 339, 340, 1000, T * P - 1]
+    assert_close(a[0, 1, toks], oa.block_attention_rows(q_mixed, k, v, rows, 0, 1, toks), "mixed waves")
+
+
+@pytest.mark.parametrize("name,steps", [("wan13b_6x", (0, 11)), ("wan14b_6x", (0,)), ("wan13b_720p_6x", (0,))],
+                         ids=["wan13b_6x", "wan14b_6x", "wan13b_720p_6x"])
+def test_workspace_full_size_sampled(gpu, name, steps):
+    w = WORKLOADS[name]
+    say("workspace full", w)
+    q, k, v = make_qkv(w, device=gpu)
+    ws = workspace_for(q, w.T)
+    rnd = random.Random(w.seed + 17)
+    heads = [0, w.H - 1]
+    host = {h: (q[:, h:h + 1].cpu(), k[:, h:h + 1].cpu(), v[:, h:h + 1].cpu()) for h in heads}
+    out = torch.empty_like(q)
+    for s in steps:
+        m = L.lvsa_build_mask(w.T, w.C, w.W, s).to(gpu)
+        L.lvsa_attention(q, k, v, m, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        rows = om.key_frames(w.T, w.C, w.W, s)
+        toks = sample_tokens(w.T, w.P, rnd)
+        got = torch.stack([out[0, h, toks].cpu() for h in heads])
+        ref = torch.stack([oa.block_attention_rows(*host[h], rows, 0, 0, toks) for h in heads])
+        assert_close(got, ref, f"ws {name} step {s}")
+        assert torch.isfinite(out).all()
+
+
 # ------------------------------- full-size workloads, sampled output rows --
 
 FULL = [

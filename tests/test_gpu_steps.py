@@ -47,15 +47,20 @@ def test_prebuilt_masks_match_per_step_masks(gpu):
             assert err <= 1e-2
 
 
-def test_graph_replay_of_the_step_sequence(gpu):
+@pytest.mark.parametrize("with_workspace", [False, True], ids=["running-max", "workspace"])
+def test_graph_replay_of_the_step_sequence(gpu, with_workspace):
+    # With a workspace each step is two kernels (key norms, attention), both
+    # captured.
     B, H, T, P, d, C, W = 1, 3, 11, 150, 128, 4, 2
-    say("graph replay", (B, H, T, P, d, C, W))
+    say("graph replay", (B, H, T, P, d, C, W), "workspace" if with_workspace else "")
     _, (qd, kd, vd) = _inputs(gpu, B, H, T, P, d, 801)
     n = 8
     ms = L.lvsa_build_mask_steps(T, C, W, 0, n).to(gpu)
+    ws = (torch.empty(L.lvsa_attention_workspace_bytes(B, H, T), dtype=torch.uint8, device=gpu)
+          if with_workspace else None)
     outs = [torch.empty_like(qd) for _ in range(n)]
     for i in range(n):
-        L.lvsa_attention(qd, kd, vd, ms.mask(i), out=outs[i])
+        L.lvsa_attention(qd, kd, vd, ms.mask(i), out=outs[i], workspace=ws)
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]
     assert not all(torch.equal(eager[0], e) for e in eager[1:])  # the steps differ
@@ -63,7 +68,7 @@ def test_graph_replay_of_the_step_sequence(gpu):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(n):
-            L.lvsa_attention(qd, kd, vd, ms.mask(i), out=outs[i])
+            L.lvsa_attention(qd, kd, vd, ms.mask(i), out=outs[i], workspace=ws)
     other = torch.empty_like(qd)
     m_other = L.lvsa_build_mask(T, C, W, 17).to(gpu)
     for rep in range(3):
