@@ -30,7 +30,9 @@
 //   max and sum are per-lane reductions plus one permlane32 swap.
 //   Online softmax in the log2 domain with a lazily updated running max
 //   (rescale only when the tile max exceeds it by more than 2^8, so exp2
-//   arguments stay <= 8 and fp32 cannot overflow).
+//   arguments stay <= 8 and fp32 cannot overflow); or, given per-frame
+//   key and value norms, no reference at all where a Cauchy-Schwarz bound
+//   keeps every exponent within ±64 (P = 2^S straight from the MFMA).
 //   Oᵀ(d × 32 queries) += Vᵀ · Pᵀ         P (bf16) comes straight from the Sᵀ
 //                                         accumulator registers; the Vᵀ
 //                                         operand is built by transposing
@@ -53,6 +55,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "lvsa_internal.h"
@@ -84,11 +87,14 @@ typedef uint16_t u16;
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
-// Largest log2 gap a fixed softmax reference may leave below a row's true
-// maximum: with the reference at most 96 above it (its bound, below), the
-// largest probability of the row stays >= 2^-96, far inside the normal
-// range of fp32 and bf16 (2^-126).
-constexpr float kMaxRefGap = 96.0f;
+// Largest bound R on |score·scale·log2e| for which a wave exponentiates its
+// scores against a fixed reference of 0: every probability then lies in
+// [2^-R, 2^R], inside the normal range of fp32 and bf16 (2^±126), and the
+// largest of a row is at least 2^-R.
+constexpr float kMaxExp = 64.0f;
+// ... provided n_keys · 2^R · max|v| stays below this, so that neither the
+// row sum nor the P·V accumulators can overflow fp32.
+constexpr float kMaxAcc = 0x1p120f;
 
 struct Args {
   const u16 *q, *k, *v;
@@ -98,9 +104,10 @@ struct Args {
   const int32_t *row_ptr, *col_idx;
   int32_t nnz, T, P, H, q_tiles, n_wg;
   float scale_log2;  // softmax scale × log2(e)
-  // Largest key norm of every (b, h, frame), [B·H·T], or null: then every
-  // wave uses the running-max softmax.
-  const float *kmax;
+  // Per (b, h, frame), [B·H·T][2]: the largest key norm max_j |k_j| and the
+  // largest value magnitude max |v_jd|; or null: then every wave uses the
+  // running-max softmax.
+  const float *fnorm;
 };
 
 // Read-only kernel inputs read at wave-uniform addresses go through the
@@ -192,7 +199,6 @@ struct Block {
 
   char *lds;
   int lane, wave, l32, hf;
-  int fixed_ref;               // the wave's reference is a fixed bound (no running max), wave-uniform
   float scale_log2;
   bf16x8_t qf[D / 16];         // the wave's Q rows, B-operand layout
   f32x16_t oacc[D / 32];       // Oᵀ accumulators (dims × 32 queries)
@@ -275,10 +281,8 @@ struct Block {
 #endif
   }
 
-  // Masks the keys >= kv of a run's tail tile, folds the tile's row maximum
-  // into m_run (raised lazily, only when it would exceed it by more than
-  // 2^kMaxLag) and rescales O and the row sum when it moves.
-  __device__ __forceinline__ void fold_max(f32x16_t (&sc)[C::KB], int kv) {
+  // Masks the keys >= kv of a run's tail tile.
+  __device__ __forceinline__ void mask_tail(f32x16_t (&sc)[C::KB], int kv) {
     if (kv < C::BN) {
       // Empty asm: keeps this wave-uniform branch a branch (no speculation
       // of the selects into every tile).
@@ -293,7 +297,12 @@ struct Block {
           if ((e >> 2) * 8 + (e & 3) >= thr) sc[kb][e] = -INFINITY;
       }
     }
-    if (fixed_ref) return;  // m_run bounds every score of the row: nothing to fold
+  }
+
+  // Folds the tile's row maximum into m_run (raised lazily, only when it
+  // would exceed it by more than 2^kMaxLag) and rescales O and the row sum
+  // when it moves.
+  __device__ __forceinline__ void fold_max(const f32x16_t (&sc)[C::KB]) {
     float mx = sc[0][0];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -313,10 +322,13 @@ struct Block {
     }
   }
 
-  // Probabilities of a tile whose maximum has been folded into m_run:
-  // P = 2^(S·scale·log2e − m_run) rounded to bf16, in the MFMA B-operand
-  // order of the P·V product; the row sum takes the same rounded values, so
-  // the normalised weights sum to one.
+  // Probabilities of a tile, rounded to bf16, in the MFMA B-operand order of
+  // the P·V product: P = 2^(S·scale·log2e − m_run) once the tile's maximum
+  // has been folded into m_run, or, with a fixed reference (FIXED), P = 2^S
+  // straight from the accumulators (the wave's Q rows are then pre-scaled by
+  // scale·log2e).  The row sum takes the same rounded values, so the
+  // normalised weights sum to one.
+  template <bool FIXED>
   __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB]) {
     const float neg_m = -m_run;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -326,7 +338,8 @@ struct Block {
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pb[kb * 2 + m][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][m * 8 + e], scale_log2, neg_m));
+          pb[kb * 2 + m][e] = (__bf16)__builtin_amdgcn_exp2f(
+              FIXED ? sc[kb][m * 8 + e] : __builtin_fmaf(sc[kb][m * 8 + e], scale_log2, neg_m));
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2_t pr = {pb[kb * 2 + m][e], pb[kb * 2 + m][e + 1]};
@@ -355,13 +368,14 @@ struct Block {
   }
 
   // One key tile from LDS buffer BUF.
-  template <int BUF>
+  template <int BUF, bool FIXED>
   __device__ __forceinline__ void tile(int kv) {
     f32x16_t sc[C::KB];
     bf16x8_t pb[2 * C::KB];
     qk<BUF>(sc);
-    fold_max(sc, kv);
-    probs(sc, pb);
+    mask_tail(sc, kv);
+    if constexpr (!FIXED) fold_max(sc);
+    probs<FIXED>(sc, pb);
     pv<BUF>(pb);
   }
 };
@@ -440,46 +454,56 @@ void lvsa_attn_fwd(Args a) {
     it.ks = it.ke = 0;
   }
 
-  // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
-  // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
-  // barrier per tile.  Unrolled by two so that every LDS offset is an
-  // immediate.
-  // ---- softmax reference.  Without a key-norm table: the running max,
-  // raised lazily.  With one: by Cauchy-Schwarz every score of query i is at
-  // most |q_i|·K, K the largest key norm over the row's frames, so
-  // m_i = scale·log2e·|q_i|·K·(1 + 2^-8) bounds every exponent by 0 (the
-  // factor covers the rounding of the fp32 norms and of the MFMA dot
-  // products) and no running max or rescale is needed.  A wave uses it only
-  // if no lane's bound is more than kMaxRefGap above that lane's true
-  // maximum (scores are >= -|q_i|·K, so 2·m_i <= kMaxRefGap suffices).
-  blk.fixed_ref = 0;
-  if (a.kmax) {
-    const const_f32p km = (const_f32p)(a.kmax + (int64_t)bh * a.T);
-    float kn = 0.f;
-    for (int32_t e = it.e; e < it.e_end; ++e) {
-      const int32_t f = it.cols[e];
-      if (f >= 0 && f < a.T) kn = fmaxf(kn, km[f]);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)blk.qf[dc][e];
-        ss = __builtin_fmaf(x, x, ss);
-      }
-    ss = swap_halves_sum(ss);  // |q_i|^2: each lane half holds half of the row
-    const float m_ref = a.scale_log2 * __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
-    const bool use = __builtin_amdgcn_ballot_w64(!(2.0f * m_ref <= kMaxRefGap)) == 0;
-    if (use) blk.m_run = m_ref;
-    blk.fixed_ref = __builtin_amdgcn_readfirstlane(use ? 1 : 0);
-  }
-
   int n_tiles = 0;
   {
     RunIter c = it;
     while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
   }
+
+  // ---- softmax reference.  Without a frame-norm table: the running max,
+  // raised lazily.  With one: by Cauchy-Schwarz every score of query i lies
+  // within ±|q_i|·K, K the largest key norm over the row's frames.  If
+  // R_i = scale·log2e·|q_i|·K·(1 + 2^-8) (the factor covers the rounding of
+  // the fp32 norms and of the MFMA dot products) is at most kMaxExp on every
+  // lane, and n_keys·2^R·max|v| below kMaxAcc, the wave pre-scales its Q rows
+  // by scale·log2e (rounded to bf16) and takes P = 2^S with no reference at
+  // all: no running max, no rescale, no subtraction.
+  bool fixed = false;
+  if (a.fnorm) {
+    const const_f32p fn = (const_f32p)(a.fnorm + (int64_t)bh * a.T * 2);
+    float kn = 0.f, vn = 0.f;
+    for (int32_t e = it.e; e < it.e_end; ++e) {
+      const int32_t f = it.cols[e];
+      if (f >= 0 && f < a.T) {
+        kn = fmaxf(kn, fn[2 * f]);
+        vn = fmaxf(vn, fn[2 * f + 1]);
+      }
+    }
+    float ss = 0.f;  // |q'_i|^2 of the scaled, rounded rows
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)(__bf16)((float)blk.qf[dc][e] * a.scale_log2);
+        ss = __builtin_fmaf(x, x, ss);
+      }
+    ss = swap_halves_sum(ss);  // each lane half holds half of the row
+    const float r_exp = __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
+    const float acc = __builtin_amdgcn_exp2f(fminf(r_exp, kMaxExp)) * (float)n_tiles * (float)C::BN * vn;
+    const bool ok = r_exp <= kMaxExp && acc < kMaxAcc;
+    fixed = __builtin_amdgcn_ballot_w64(!ok) == 0;
+    if (fixed) {
+#pragma unroll
+      for (int dc = 0; dc < D / 16; ++dc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) blk.qf[dc][e] = (__bf16)((float)blk.qf[dc][e] * a.scale_log2);
+    }
+  }
+
+  // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
+  // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
+  // barrier per tile.  Unrolled by two so that every LDS offset is an
+  // immediate.
   int pos = 0, kv = 0;
   auto advance = [&]() {  // next tile, moving to the next run when needed
     pos += C::BN;
@@ -501,23 +525,32 @@ void lvsa_attn_fwd(Args a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int i = 0; i + 1 < n_tiles; i += 2) {
-    const int kv0 = kv;
-    advance();  // tile i+1 -> buffer 1
-    issue(1);
-    if (compute) blk.template tile<0>(kv0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int kv1 = kv;
-    if (i + 2 < n_tiles) {  // tile i+2 -> buffer 0
-      advance();
-      issue(0);
+  // The loop is instantiated once per softmax mode; every wave of the
+  // workgroup runs the same loads and barriers in either.
+  auto run = [&](auto fixed_c) {
+    constexpr bool F = decltype(fixed_c)::value;
+    for (int i = 0; i + 1 < n_tiles; i += 2) {
+      const int kv0 = kv;
+      advance();  // tile i+1 -> buffer 1
+      issue(1);
+      if (compute) blk.template tile<0, F>(kv0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int kv1 = kv;
+      if (i + 2 < n_tiles) {  // tile i+2 -> buffer 0
+        advance();
+        issue(0);
+      }
+      if (compute) blk.template tile<1, F>(kv1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
-    if (compute) blk.template tile<1>(kv1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  if ((n_tiles & 1) && compute) blk.template tile<0>(kv);
+    if ((n_tiles & 1) && compute) blk.template tile<0, F>(kv);
+  };
+  if (fixed)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // ---- epilogue: normalise, round to bf16, store
   {
@@ -540,37 +573,53 @@ void lvsa_attn_fwd(Args a) {
   }
 }
 
-// Largest key norm of one (b, h, frame): one workgroup per frame streams its
-// P key rows once (16 bytes per lane, D/8 lanes per row) and writes
-// max_j |k_j| (fp32 sums of squares of the bf16 values) to kmax[(b·H + h)·T + t].
+// Norms of one (b, h, frame): one workgroup per frame streams its P key and
+// value rows once (16 bytes per lane, D/8 lanes per row) and writes
+// max_j |k_j| (from fp32 sums of squares of the bf16 values) and max |v_jd|
+// to fnorm[((b·H + h)·T + t)·2 + {0, 1}].
 template <int D>
-__global__ __launch_bounds__(256) void lvsa_key_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
-                                                      int32_t H, int32_t T, int32_t P, float *kmax) {
-  constexpr int LPR = D / 8;          // lanes per key row
+__global__ __launch_bounds__(256) void lvsa_frame_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
+                                                        const u16 *v, int64_t v_sb, int64_t v_sh, int32_t v_sn,
+                                                        int32_t H, int32_t T, int32_t P, float *fnorm) {
+  constexpr int LPR = D / 8;          // lanes per row
   constexpr int RPI = 256 / LPR;      // rows per workgroup iteration
   const int item = blockIdx.x;        // (b·H + h)·T + t
   const int t = item % T;
   const int bh = item / T;
   const int h = bh % H;
   const int b = bh / H;
-  const u16 *base = k + (int64_t)b * k_sb + (int64_t)h * k_sh + (int64_t)t * P * k_sn;
+  const u16 *kb = k + (int64_t)b * k_sb + (int64_t)h * k_sh + (int64_t)t * P * k_sn;
+  const u16 *vb = v + (int64_t)b * v_sb + (int64_t)h * v_sh + (int64_t)t * P * v_sn;
   const int col = (threadIdx.x % LPR) * 8;
-  float best = 0.f;
+  float kbest = 0.f, vbest = 0.f;
   for (int r = threadIdx.x / LPR; r < P; r += RPI) {
-    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(base + (int64_t)r * k_sn + col);
+    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(kb + (int64_t)r * k_sn + col);
+    const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(vb + (int64_t)r * v_sn + col);
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf((float)x[e], (float)x[e], ss);
+    for (int e = 0; e < 8; ++e) {
+      ss = __builtin_fmaf((float)x[e], (float)x[e], ss);
+      vbest = fmaxf(vbest, __builtin_fabsf((float)y[e]));
+    }
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);  // the row's LPR lanes
-    best = fmaxf(best, ss);
+    kbest = fmaxf(kbest, ss);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
-  __shared__ float wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+  for (int o = 32; o > 0; o >>= 1) {
+    kbest = fmaxf(kbest, __shfl_xor(kbest, o));
+    vbest = fmaxf(vbest, __shfl_xor(vbest, o));
+  }
+  __shared__ float wk[4], wv[4];
+  if ((threadIdx.x & 63) == 0) {
+    wk[threadIdx.x >> 6] = kbest;
+    wv[threadIdx.x >> 6] = vbest;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) kmax[item] = __builtin_sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  if (threadIdx.x == 0) {
+    fnorm[2 * item] = __builtin_sqrtf(fmaxf(fmaxf(wk[0], wk[1]), fmaxf(wk[2], wk[3])));
+    fnorm[2 * item + 1] = fmaxf(fmaxf(wv[0], wv[1]), fmaxf(wv[2], wv[3]));
+  }
 }
 
 // ------------------------------------------------------------------ host --
@@ -652,12 +701,13 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
 
 template <int D, int NW>
 int launch(const Args &args, hipStream_t stream) {
-  if (args.kmax) {
-    // the key-norm table first, on the same stream
-    hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
-                       args.k_sh, args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.kmax));
+  if (args.fnorm) {
+    // the frame-norm table first, on the same stream
+    hipLaunchKernelGGL((lvsa_frame_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
+                       args.k_sh, args.k_sn, args.v, args.v_sb, args.v_sh, args.v_sn, args.H, args.T, args.P,
+                       const_cast<float *>(args.fnorm));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "key-norm kernel launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "frame-norm kernel launch failed: %s", hipGetErrorString(e));
   }
   hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
@@ -666,7 +716,7 @@ int launch(const Args &args, hipStream_t stream) {
 }
 
 int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t T) {
-  return ((B * H * T * (int64_t)sizeof(float) + 255) / 256) * 256;
+  return ((B * H * T * 2 * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
 
 int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
@@ -738,7 +788,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   a.n_wg = (int32_t)n_wg;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  a.kmax = use_ws ? static_cast<const float *>(workspace) : nullptr;
+  a.fnorm = use_ws ? static_cast<const float *>(workspace) : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) return launch<128, NW>(a, s);

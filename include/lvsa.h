@@ -194,8 +194,8 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
                    void *stream);
 
-/* Bytes of device workspace lvsa_attention_ws needs for B, H and T: one
- * float per (b, h, frame), rounded up to 256.  Errors: LVSA_ERR_ARG. */
+/* Bytes of device workspace lvsa_attention_ws needs for B, H and T: two
+ * floats per (b, h, frame), rounded up to 256.  Errors: LVSA_ERR_ARG. */
 int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes);
 
 /* lvsa_attention with a caller-provided device workspace, used to drop the
@@ -203,15 +203,16 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *byt
  *
  * Source: the same computation as lvsa_attention (gist.science explainer,
  * Technical Summary §2).  The workspace changes only the softmax's reference
- * point, which cancels in the normalisation: a first kernel writes the
- * largest key norm of every (b, h, frame) to the workspace; then, by
- * Cauchy-Schwarz, scale·|q_i|·(largest key norm over A(t)) bounds every
- * score of query i, and a wave whose 64 lanes all have bounds close enough
- * to their true maxima (within 2^96 in probability) uses that bound as a
- * fixed reference -- no running maximum, no rescaling.  Other waves (large
- * query/key norms) keep the running-maximum path.  Results agree with
- * lvsa_attention to the same accuracy, not bit for bit (the probabilities
- * are rounded to bf16 at a different scale).
+ * point, which cancels in the normalisation: a first kernel writes, for every
+ * (b, h, frame), the largest key norm and the largest |value| element to the
+ * workspace.  By Cauchy-Schwarz, R_i = scale·log2(e)·|q_i|·(largest key norm
+ * over A(t)) bounds |score·log2(e)| of query i; a wave whose 64 lanes all have
+ * R_i <= 64, and whose unnormalised sums cannot overflow fp32 (keys·2^R·
+ * max|v| < 2^120), exponentiates its scores with no reference at all -- no
+ * running maximum, no rescaling, no subtraction (its Q rows are pre-scaled
+ * by scale·log2(e) and rounded to bf16).  Other waves keep the
+ * running-maximum path of lvsa_attention, bit for bit.  Results agree with
+ * lvsa_attention to the same accuracy, not bit for bit.
  *
  * Arguments as lvsa_attention, plus:
  *   workspace        : device memory of at least

@@ -185,9 +185,9 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
 
 
 def test_workspace_bytes():
-    assert L.lvsa_attention_workspace_bytes(1, 12, 121) == 5888  # 1452 floats, rounded up to 256 bytes
+    assert L.lvsa_attention_workspace_bytes(1, 12, 121) == 11776  # 1452 frames x 2 floats, rounded up to 256 bytes
     assert L.lvsa_attention_workspace_bytes(1, 2, 8) == 256
-    assert L.lvsa_attention_workspace_bytes(2, 40, 121) == 38912
+    assert L.lvsa_attention_workspace_bytes(2, 40, 121) == 77568
     lib = L.library()
     n = ctypes.c_int64(0)
     assert lib.lvsa_attention_workspace_bytes(0, 2, 8, ctypes.byref(n)) == L.LVSA_ERR_ARG
@@ -209,7 +209,7 @@ def test_workspace_errors_are_reported_before_any_device_work():
     assert _attn_ws(q, k, v, o, 0, 256) == L.LVSA_ERR_ARG                 # NULL
     assert "NULL" in L.lvsa_last_error()
     assert _attn_ws(q, k, v, o, ws + 2, 256) == L.LVSA_ERR_ARG            # misaligned
-    assert _attn_ws(q, k, v, o, ws, 255) == L.LVSA_ERR_CAPACITY           # 2·8 floats -> 256 bytes
+    assert _attn_ws(q, k, v, o, ws, 255) == L.LVSA_ERR_CAPACITY           # 2·8·2 floats -> 256 bytes
     assert _attn_ws(q, k, v, o, base + 16, 256) == L.LVSA_ERR_ARG         # inside q
     assert "overlaps" in L.lvsa_last_error()
     assert _attn_ws(_rec(base, dtype=0), k, v, o, ws, 256) == L.LVSA_ERR_DTYPE  # the plain checks still apply
