@@ -108,6 +108,9 @@ struct Args {
   // largest value magnitude max |v_jd|; or null: then every wave uses the
   // running-max softmax.
   const float *fnorm;
+  // Per-XCD work-item counters, zeroed before the launch, or null: then
+  // workgroup i runs the (i mod 8)-th XCD's (i div 8)-th item.
+  int *tickets;
 };
 
 // Read-only kernel inputs read at wave-uniform addresses go through the
@@ -395,13 +398,52 @@ void lvsa_attn_fwd(Args a) {
   blk.hf = blk.lane >> 5;
   blk.scale_log2 = a.scale_log2;
 
-  // ---- work item (XCD-contiguous remap of the dispatch order)
+  // ---- work item.  The items are split into 8 contiguous ranges, one per
+  // XCD, so that the query tiles of a frame and neighbouring frames (which
+  // share most key frames) run on one XCD and share its L2.  Statically,
+  // workgroup i runs the (i div 8)-th item of XCD i mod 8's range (the
+  // dispatcher deals workgroups round-robin over the XCDs).  With ticket
+  // counters, a workgroup takes the next item of the range of the XCD it
+  // runs on, and once that range is used up, of the others: the XCDs of one
+  // part run at different speeds (up to ~7% apart), and a static split
+  // leaves the fast ones idle while the slowest finishes.  More workgroups
+  // than items are launched; the ones that find no item left exit.
+  auto xcd_range = [&](int x, int *base, int *cnt) {
+    const int n = a.n_wg, per = n / kNumXcd, rem = n % kNumXcd;
+    *base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+    *cnt = per + (x < rem ? 1 : 0);
+  };
   int item;
-  {
-    const int bid = blockIdx.x, n = a.n_wg;
-    const int x = bid % kNumXcd, j = bid / kNumXcd;
-    const int per = n / kNumXcd, rem = n % kNumXcd;
-    item = (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+  if (a.tickets) {
+    // The item is broadcast through the first word of LDS tile buffer 1: the
+    // first tile loads (buffer 0) do not touch it, and every wave reads it
+    // before the barrier that precedes the loads into buffer 1.  (A separate
+    // __shared__ word would take the workgroup past 32 KiB of LDS, which
+    // measured 2.5-6% slower.)
+    int *const s_item = reinterpret_cast<int *>(lds + 2 * C::TILE_BYTES);
+    if (tid == 0) {
+      unsigned xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      int got = -1;
+      for (int d = 0; d < kNumXcd && got < 0; ++d) {
+        const int x = (int)((xcc + d) % kNumXcd);
+        int base, cnt;
+        xcd_range(x, &base, &cnt);
+        // system scope: performed past the per-XCD L2s, so every XCD sees
+        // one counter
+        const int k = __hip_atomic_fetch_add(a.tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (k < cnt) got = base + k;
+      }
+      *s_item = got;
+    }
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(*s_item);
+    if (item < 0) return;  // every item is taken (uniform: all waves leave)
+  } else {
+    const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+    int base, cnt;
+    xcd_range(x, &base, &cnt);
+    item = base + j;
   }
   const int qt = item % a.q_tiles;
   const int rest = item / a.q_tiles;
@@ -576,11 +618,15 @@ void lvsa_attn_fwd(Args a) {
 // Norms of one (b, h, frame): one workgroup per frame streams its P key and
 // value rows once (16 bytes per lane, D/8 lanes per row) and writes
 // max_j |k_j| (from fp32 sums of squares of the bf16 values) and max |v_jd|
-// to fnorm[((b·H + h)·T + t)·2 + {0, 1}].
+// to fnorm[((b·H + h)·T + t)·2 + {0, 1}].  Workgroup 0 also zeroes the
+// attention kernel's 8 ticket counters.
 template <int D>
 __global__ __launch_bounds__(256) void lvsa_frame_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
                                                         const u16 *v, int64_t v_sb, int64_t v_sh, int32_t v_sn,
-                                                        int32_t H, int32_t T, int32_t P, float *fnorm) {
+                                                        int32_t H, int32_t T, int32_t P, float *fnorm,
+                                                        int *tickets) {
+  if (blockIdx.x == 0 && threadIdx.x < kNumXcd)  // for the attention launch that follows
+    __hip_atomic_store(tickets + threadIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   constexpr int LPR = D / 8;          // lanes per row
   constexpr int RPI = 256 / LPR;      // rows per workgroup iteration
   const int item = blockIdx.x;        // (b·H + h)·T + t
@@ -705,19 +751,25 @@ int launch(const Args &args, hipStream_t stream) {
     // the frame-norm table first, on the same stream
     hipLaunchKernelGGL((lvsa_frame_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
                        args.k_sh, args.k_sn, args.v, args.v_sb, args.v_sh, args.v_sn, args.H, args.T, args.P,
-                       const_cast<float *>(args.fnorm));
+                       const_cast<float *>(args.fnorm), args.tickets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "frame-norm kernel launch failed: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3(args.n_wg), dim3(NW * 64), 0, stream, args);
+  // With tickets: 1/8 more workgroups than items, so that the fastest XCD
+  // can take over up to that share of the others' items.
+  const int64_t grid = args.tickets ? args.n_wg + args.n_wg / 8 + kNumXcd : args.n_wg;
+  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return lvsa::ok();
 }
 
-int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t T) {
+// Workspace: the frame-norm table (B·H·T float pairs), then, at the next
+// 256-byte boundary, the 8 ticket counters (256 bytes).
+int64_t norms_bytes_for(int64_t B, int64_t H, int64_t T) {
   return ((B * H * T * 2 * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
+int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t T) { return norms_bytes_for(B, H, T) + 256; }
 
 int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
                    const int32_t *row_ptr_dev, const int32_t *col_idx_dev, int32_t T, int32_t nnz,
@@ -767,7 +819,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   const int BM = NW * 32;
   const int q_tiles = (P + BM - 1) / BM;
   const int64_t n_wg = (int64_t)q->B * q->H * T * q_tiles;
-  if (n_wg > INT32_MAX) return lvsa::fail(LVSA_ERR_SHAPE, "grid of %lld workgroups too large", (long long)n_wg);
+  if (n_wg > INT32_MAX / 2) return lvsa::fail(LVSA_ERR_SHAPE, "grid of %lld workgroups too large", (long long)n_wg);
 
   Args a;
   a.q = static_cast<const u16 *>(q->data);
@@ -789,6 +841,8 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
   a.fnorm = use_ws ? static_cast<const float *>(workspace) : nullptr;
+  a.tickets = use_ws ? reinterpret_cast<int *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T))
+                     : nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) return launch<128, NW>(a, s);

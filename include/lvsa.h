@@ -195,7 +195,8 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    void *stream);
 
 /* Bytes of device workspace lvsa_attention_ws needs for B, H and T: two
- * floats per (b, h, frame), rounded up to 256.  Errors: LVSA_ERR_ARG. */
+ * floats per (b, h, frame), rounded up to 256, plus 256 bytes of work
+ * counters.  Errors: LVSA_ERR_ARG. */
 int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes);
 
 /* lvsa_attention with a caller-provided device workspace, used to drop the
@@ -213,6 +214,12 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *byt
  * by scale·log2(e) and rounded to bf16).  Other waves keep the
  * running-maximum path of lvsa_attention, bit for bit.  Results agree with
  * lvsa_attention to the same accuracy, not bit for bit.
+ *
+ * The workspace also holds one work counter per XCD: workgroups take their
+ * (b, h, frame, query tile) items from counters instead of a fixed split,
+ * so that faster XCDs take over items of slower ones.  Which workgroup
+ * computes an item does not change its result: outputs are bitwise
+ * reproducible from call to call.
  *
  * Arguments as lvsa_attention, plus:
  *   workspace        : device memory of at least

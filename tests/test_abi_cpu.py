@@ -185,9 +185,10 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
 
 
 def test_workspace_bytes():
-    assert L.lvsa_attention_workspace_bytes(1, 12, 121) == 11776  # 1452 frames x 2 floats, rounded up to 256 bytes
-    assert L.lvsa_attention_workspace_bytes(1, 2, 8) == 256
-    assert L.lvsa_attention_workspace_bytes(2, 40, 121) == 77568
+    # 1452 frames x 2 floats rounded up to 256 bytes, then 256 bytes of counters
+    assert L.lvsa_attention_workspace_bytes(1, 12, 121) == 11776 + 256
+    assert L.lvsa_attention_workspace_bytes(1, 2, 8) == 512
+    assert L.lvsa_attention_workspace_bytes(2, 40, 121) == 77568 + 256
     lib = L.library()
     n = ctypes.c_int64(0)
     assert lib.lvsa_attention_workspace_bytes(0, 2, 8, ctypes.byref(n)) == L.LVSA_ERR_ARG
@@ -206,13 +207,15 @@ def test_workspace_errors_are_reported_before_any_device_work():
     sz = 2 * 512 * 64 * 2
     q, k, v, o = (_rec(base + i * sz) for i in range(4))
     ws = base + 8 * sz
-    assert _attn_ws(q, k, v, o, 0, 256) == L.LVSA_ERR_ARG                 # NULL
+    need = L.lvsa_attention_workspace_bytes(1, 2, 8)  # 2·8·2 floats -> 256 bytes, + 256 of counters
+    assert need == 512
+    assert _attn_ws(q, k, v, o, 0, need) == L.LVSA_ERR_ARG                # NULL
     assert "NULL" in L.lvsa_last_error()
-    assert _attn_ws(q, k, v, o, ws + 2, 256) == L.LVSA_ERR_ARG            # misaligned
-    assert _attn_ws(q, k, v, o, ws, 255) == L.LVSA_ERR_CAPACITY           # 2·8·2 floats -> 256 bytes
-    assert _attn_ws(q, k, v, o, base + 16, 256) == L.LVSA_ERR_ARG         # inside q
+    assert _attn_ws(q, k, v, o, ws + 2, need) == L.LVSA_ERR_ARG           # misaligned
+    assert _attn_ws(q, k, v, o, ws, need - 1) == L.LVSA_ERR_CAPACITY      # too small
+    assert _attn_ws(q, k, v, o, base + 16, need) == L.LVSA_ERR_ARG        # inside q
     assert "overlaps" in L.lvsa_last_error()
-    assert _attn_ws(_rec(base, dtype=0), k, v, o, ws, 256) == L.LVSA_ERR_DTYPE  # the plain checks still apply
+    assert _attn_ws(_rec(base, dtype=0), k, v, o, ws, need) == L.LVSA_ERR_DTYPE  # the plain checks still apply
 
 
 def test_attention_rejects_self_overlapping_output():
