@@ -44,11 +44,12 @@
 // workgroup barrier per tile.  16-byte chunks are XOR-swizzled by key so
 // every MFMA operand read is bank-conflict free.
 //
-// Launch order.  Workgroups are dispatched round-robin over the 8 XCDs; the
-// block index is remapped so each XCD receives a contiguous range of
-// (b, h, t, query-tile) work items: the query tiles of a frame and
-// neighbouring frames (which share most of their key frames) run on the same
-// XCD and hit in its L2.
+// Launch order.  Workgroups are dispatched round-robin over the 8 XCDs; each
+// XCD receives a contiguous range of (b, h, t, query-tile) work items: the
+// query tiles of a frame and neighbouring frames (which share most of their
+// key frames) run on the same XCD and hit in its L2.  With a workspace the
+// items are taken from per-XCD counters, so XCDs that clock faster take over
+// work from slower ones (see the work-item block in the kernel).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
