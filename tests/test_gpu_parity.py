@@ -305,7 +305,7 @@ def test_workspace_mid_size(gpu, case):
         assert_close(o, o_exact.double().cpu(), f"ws vs exact path, step {s}")
 
 
-def test_workspace_takes_the_fixed_reference_and_falls_back_on_large_norms_or_values(gpu):
+def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(gpu):
     # Unit-variance d=128 inputs: every wave's bound is close enough, so the
     # reference-free path is used (outputs round differently from the running-max
     # path).  Keys shifted by a large common vector make |q|·max|k| far above
