@@ -171,7 +171,7 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
     recs = [L._tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
     # With a workspace the call is lvsa_attention_ws: a frame-norm pass, then
     # the attention without a softmax reference where the bound allows.
-    ws_bytes = L.lvsa_attention_workspace_bytes(w.B, w.H, T) if workspace else 0
+    ws_bytes = L.lvsa_attention_workspace_bytes(w.B, w.H, T * w.P, w.D, T) if workspace else 0
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     def attention(rp_ptr, ci_ptr, sptr):
@@ -392,7 +392,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_frame_norms<128> in the timed call)"
+            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_frame_norms<128> and lvsa_combine<128,4> in the timed call)"
                                                 if not args.no_workspace else ""),
             "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
 

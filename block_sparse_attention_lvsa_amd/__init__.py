@@ -18,7 +18,7 @@ Functions with the ABI's names:
   lvsa_validate_mask(T, row_ptr, col_idx)
   lvsa_attention(q, k, v, mask_dev, out=None, scale=None, stream=None, workspace=None) -> out
       (with a workspace: the C ABI's lvsa_attention_ws)
-  lvsa_attention_workspace_bytes(B, H, T) -> int
+  lvsa_attention_workspace_bytes(B, H, N, D, T) -> int
 
 ``Mask.to(device)`` copies the CSR arrays (``non_blocking`` on the current
 stream) for ``lvsa_attention``.  ``MaskSteps`` holds the masks of a run of
@@ -111,7 +111,8 @@ def library() -> ctypes.CDLL:
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.POINTER(LvsaTensor), ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.lvsa_attention_workspace_bytes.restype = ctypes.c_int
-        lib.lvsa_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+        lib.lvsa_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int64, ctypes.c_int32,
                                                        ctypes.POINTER(ctypes.c_int64)]
         _LIB = lib
     return _LIB
@@ -242,10 +243,11 @@ def _tensor_record(x, name: str) -> LvsaTensor:
                       LVSA_DTYPE_BF16 if x.dtype == torch.bfloat16 else 0)
 
 
-def lvsa_attention_workspace_bytes(B: int, H: int, T: int) -> int:
-    """Device workspace bytes lvsa_attention needs when given a workspace."""
+def lvsa_attention_workspace_bytes(B: int, H: int, N: int, D: int, T: int) -> int:
+    """Device workspace bytes lvsa_attention needs when given a workspace, for
+    [B, H, N, D] tensors of T frames."""
     n = ctypes.c_int64(0)
-    _check(library().lvsa_attention_workspace_bytes(B, H, T, ctypes.byref(n)))
+    _check(library().lvsa_attention_workspace_bytes(B, H, N, D, T, ctypes.byref(n)))
     return n.value
 
 
@@ -254,7 +256,7 @@ def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None,
 
     q, k, v, out: [B, H, T·P, D] bf16 CUDA tensors; mask: a Mask whose
     arrays are already on q's device.  ``workspace``: optional device tensor
-    of at least lvsa_attention_workspace_bytes(B, H, T) bytes (then the call
+    of at least lvsa_attention_workspace_bytes(B, H, N, D, T) bytes (then the call
     is the ABI's lvsa_attention_ws).  Launches on ``stream`` (default: the
     current stream) and returns ``out`` without synchronising.
     """

@@ -52,6 +52,7 @@
 // work from slower ones (see the work-item block in the kernel).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -112,6 +113,12 @@ struct Args {
   // Per-XCD work-item counters, zeroed before the launch, or null: then
   // workgroup i runs the (i mod 8)-th XCD's (i div 8)-th item.
   int *tickets;
+  // With tickets: the last min(split_cap, range / 4) items of each XCD
+  // range run as two halves of their CSR row, whose partial results (records
+  // of kPartialFloats(D) floats per lane, slot x·split_cap + j) go to
+  // `partial` and are merged by lvsa_combine; split_cap = 0 splits nothing.
+  float *partial;
+  int32_t split_cap;
 };
 
 // Read-only kernel inputs read at wave-uniform addresses go through the
@@ -193,6 +200,22 @@ typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 
 // Word 3 of a raw buffer descriptor (CDNA: 32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
+
+// The items are split into 8 contiguous ranges, one per XCD.
+__device__ __forceinline__ void xcd_range(int n, int x, int *base, int *cnt) {
+  const int per = n / kNumXcd, rem = n % kNumXcd;
+  *base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  *cnt = per + (x < rem ? 1 : 0);
+}
+
+// Items of one XCD range run as two halves (the end of the range, where the
+// last workgroups of a launch finish at different times; shorter items make
+// that ragged end shorter).
+__device__ __forceinline__ int split_count(int cap, int cnt) { return min(cap, cnt / 4); }
+
+// Floats per lane in a partial record: the lane's O accumulators (D/2),
+// its partial row sum, the row's reference, padding to 16 bytes.
+__host__ __device__ constexpr int kPartialFloats(int d) { return d / 2 + 4; }
 
 // One wave's state and steps.  Kept in a struct so that the per-tile step
 // can be specialised on the LDS buffer (immediate LDS offsets).  A wave owns
@@ -409,41 +432,51 @@ void lvsa_attn_fwd(Args a) {
   // part run at different speeds (up to ~7% apart), and a static split
   // leaves the fast ones idle while the slowest finishes.  More workgroups
   // than items are launched; the ones that find no item left exit.
-  auto xcd_range = [&](int x, int *base, int *cnt) {
-    const int n = a.n_wg, per = n / kNumXcd, rem = n % kNumXcd;
-    *base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
-    *cnt = per + (x < rem ? 1 : 0);
-  };
-  int item;
+  int item, half = -1, slot = 0;
   if (a.tickets) {
-    // The item is broadcast through the first word of LDS tile buffer 1: the
-    // first tile loads (buffer 0) do not touch it, and every wave reads it
-    // before the barrier that precedes the loads into buffer 1.  (A separate
+    // The item (and, for a half, which half and its record slot) is
+    // broadcast through the first words of LDS tile buffer 1: the first tile
+    // loads (buffer 0) do not touch them, and every wave reads them before
+    // the barrier that precedes the loads into buffer 1.  (A separate
     // __shared__ word would take the workgroup past 32 KiB of LDS, which
     // measured 2.5-6% slower.)
     int *const s_item = reinterpret_cast<int *>(lds + 2 * C::TILE_BYTES);
     if (tid == 0) {
       unsigned xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-      int got = -1;
+      int got = -1, gh = -1, gs = 0;
       for (int d = 0; d < kNumXcd && got < 0; ++d) {
         const int x = (int)((xcc + d) % kNumXcd);
         int base, cnt;
-        xcd_range(x, &base, &cnt);
+        xcd_range(a.n_wg, x, &base, &cnt);
+        // A range hands out cnt + S tickets: its first cnt - S items whole,
+        // then each of its last S items as two halves.
+        const int S = split_count(a.split_cap, cnt), whole = cnt - S;
         // system scope: performed past the per-XCD L2s, so every XCD sees
         // one counter
         const int k = __hip_atomic_fetch_add(a.tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        if (k < cnt) got = base + k;
+        if (k < whole) {
+          got = base + k;
+        } else if (k < cnt + S) {
+          const int j = (k - whole) >> 1;
+          got = base + whole + j;
+          gh = (k - whole) & 1;
+          gs = x * a.split_cap + j;
+        }
       }
-      *s_item = got;
+      s_item[0] = got;
+      s_item[1] = gh;
+      s_item[2] = gs;
     }
     __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(*s_item);
+    item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    half = __builtin_amdgcn_readfirstlane(s_item[1]);
+    slot = __builtin_amdgcn_readfirstlane(s_item[2]);
     if (item < 0) return;  // every item is taken (uniform: all waves leave)
   } else {
     const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
     int base, cnt;
-    xcd_range(x, &base, &cnt);
+    xcd_range(a.n_wg, x, &base, &cnt);
     item = base + j;
   }
   const int qt = item % a.q_tiles;
@@ -483,9 +516,11 @@ void lvsa_attn_fwd(Args a) {
 
   // ---- CSR row -> runs of key frames
   RunIter it;
+  int32_t rb, re;  // the whole CSR row
   {
     const const_i32p rp = (const_i32p)a.row_ptr;
-    int32_t rb = rp[t], re = rp[t + 1];
+    rb = rp[t];
+    re = rp[t + 1];
     rb = rb < 0 ? 0 : (rb > a.nnz ? a.nnz : rb);
     re = re < rb ? rb : (re > a.nnz ? a.nnz : re);
     it.cols = (const_i32p)a.col_idx;
@@ -496,11 +531,31 @@ void lvsa_attn_fwd(Args a) {
     it.last = -1;
     it.ks = it.ke = 0;
   }
-
-  int n_tiles = 0;
+  int n_tiles = 0;  // tiles of the whole row
   {
     RunIter c = it;
     while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
+  }
+  int n_walk = n_tiles;  // tiles this workgroup walks
+  if (half >= 0) {
+    // A half walks entries [rb, mid) or [mid, re) of the row, the second
+    // starting from the walk's state at mid, so that together they keep
+    // exactly the entries the whole walk keeps.
+    const int32_t mid = rb + (re - rb) / 2;
+    RunIter c = it;
+    c.e_end = mid;
+    int first = 0;
+    while (c.next_run()) first += (c.ke - c.ks + C::BN - 1) / C::BN;
+    if (half == 0) {
+      it.e_end = mid;
+      n_walk = first;
+    } else {
+      it.e = mid;
+      it.last = c.last;
+      n_walk = 0;
+      RunIter d = it;
+      while (d.next_run()) n_walk += (d.ke - d.ks + C::BN - 1) / C::BN;
+    }
   }
 
   // ---- softmax reference.  Without a frame-norm table: the running max,
@@ -515,7 +570,7 @@ void lvsa_attn_fwd(Args a) {
   if (a.fnorm) {
     const const_f32p fn = (const_f32p)(a.fnorm + (int64_t)bh * a.T * 2);
     float kn = 0.f, vn = 0.f;
-    for (int32_t e = it.e; e < it.e_end; ++e) {
+    for (int32_t e = rb; e < re; ++e) {  // the whole row, so both halves decide alike
       const int32_t f = it.cols[e];
       if (f >= 0 && f < a.T) {
         kn = fmaxf(kn, fn[2 * f]);
@@ -536,6 +591,7 @@ void lvsa_attn_fwd(Args a) {
     const bool ok = r_exp <= kMaxExp && acc < kMaxAcc;
     fixed = __builtin_amdgcn_ballot_w64(!ok) == 0;
     if (fixed) {
+      blk.m_run = 0.f;  // the reference is 0 (a partial record carries it)
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
@@ -560,7 +616,7 @@ void lvsa_attn_fwd(Args a) {
     blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
     blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
   };
-  if (n_tiles > 0) {
+  if (n_walk > 0) {
     it.next_run();
     pos = it.ks;
     kv = min(C::BN, it.ke - pos);
@@ -572,7 +628,7 @@ void lvsa_attn_fwd(Args a) {
   // workgroup runs the same loads and barriers in either.
   auto run = [&](auto fixed_c) {
     constexpr bool F = decltype(fixed_c)::value;
-    for (int i = 0; i + 1 < n_tiles; i += 2) {
+    for (int i = 0; i + 1 < n_walk; i += 2) {
       const int kv0 = kv;
       advance();  // tile i+1 -> buffer 1
       issue(1);
@@ -580,7 +636,7 @@ void lvsa_attn_fwd(Args a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       const int kv1 = kv;
-      if (i + 2 < n_tiles) {  // tile i+2 -> buffer 0
+      if (i + 2 < n_walk) {  // tile i+2 -> buffer 0
         advance();
         issue(0);
       }
@@ -588,12 +644,30 @@ void lvsa_attn_fwd(Args a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if ((n_tiles & 1) && compute) blk.template tile<0, F>(kv);
+    if ((n_walk & 1) && compute) blk.template tile<0, F>(kv);
   };
   if (fixed)
     run(std::true_type{});
   else
     run(std::false_type{});
+
+  // ---- a half writes its partial record (unnormalised O, partial row sum,
+  // reference) for lvsa_combine, which runs after this kernel
+  if (half >= 0) {
+    if (compute) {
+      constexpr int R4 = kPartialFloats(D) / 4;
+      float4 *rec = reinterpret_cast<float4 *>(a.partial) +
+                    ((int64_t)(slot * 2 + half) * NW + blk.wave) * R4 * 64 + blk.lane;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rec[(i * 4 + j) * 64] = make_float4(blk.oacc[i][j * 4], blk.oacc[i][j * 4 + 1], blk.oacc[i][j * 4 + 2],
+                                              blk.oacc[i][j * 4 + 3]);
+      rec[(R4 - 1) * 64] = make_float4(blk.l_run, blk.m_run, 0.f, 0.f);
+    }
+    return;
+  }
 
   // ---- epilogue: normalise, round to bf16, store
   {
@@ -667,6 +741,58 @@ __global__ __launch_bounds__(256) void lvsa_frame_norms(const u16 *k, int64_t k_
     fnorm[2 * item] = __builtin_sqrtf(fmaxf(fmaxf(wk[0], wk[1]), fmaxf(wk[2], wk[3])));
     fnorm[2 * item + 1] = fmaxf(fmaxf(wv[0], wv[1]), fmaxf(wv[2], wv[3]));
   }
+}
+
+// Merges the two halves of every split item: one workgroup per record slot,
+// one wave per 32 query rows as in lvsa_attn_fwd.  Each lane reads its two
+// partial records (O accumulators, partial row sum l and reference m of its
+// query), rescales both to the larger reference, adds, normalises and
+// stores the item's output rows.  Runs after lvsa_attn_fwd on the same
+// stream, so the records are complete.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void lvsa_combine(Args a) {
+  const int x = blockIdx.x / a.split_cap, j = blockIdx.x % a.split_cap;
+  int base, cnt;
+  xcd_range(a.n_wg, x, &base, &cnt);
+  const int S = split_count(a.split_cap, cnt);
+  if (j >= S) return;
+  const int item = base + (cnt - S) + j;
+  const int qt = item % a.q_tiles;
+  const int rest = item / a.q_tiles;
+  const int t = rest % a.T;
+  const int bh = rest / a.T;
+  const int h = bh % a.H;
+  const int b = bh / a.H;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = qt * NW * 32 + wave * 32;
+  if (row0 >= a.P) return;  // a wave with no rows wrote no record
+  constexpr int R4 = kPartialFloats(D) / 4;
+  const float4 *r0 = reinterpret_cast<const float4 *>(a.partial) + ((int64_t)(blockIdx.x * 2) * NW + wave) * R4 * 64 + lane;
+  const float4 *r1 = r0 + (int64_t)NW * R4 * 64;
+  const float4 t0 = r0[(R4 - 1) * 64], t1 = r1[(R4 - 1) * 64];
+  // weights 2^(m_h - m); a half that saw no key has m_h = -inf and weight 0
+  const float m = fmaxf(t0.y, t1.y);
+  const float w0 = t0.y == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t0.y - m);
+  const float w1 = t1.y == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t1.y - m);
+  const float l = w0 * t0.x + w1 * t1.x;
+  const float l_tot = swap_halves_sum(l);
+  const int r = row0 + (lane & 31);
+  if (r >= a.P) return;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * a.P + r) * a.o_sn;
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 o0 = r0[(dc * 4 + i) * 64], o1 = r1[(dc * 4 + i) * 64];
+      bf16x4_t o4;
+      o4[0] = (__bf16)((w0 * o0.x + w1 * o1.x) * inv);
+      o4[1] = (__bf16)((w0 * o0.y + w1 * o1.y) * inv);
+      o4[2] = (__bf16)((w0 * o0.z + w1 * o1.z) * inv);
+      o4[3] = (__bf16)((w0 * o0.w + w1 * o1.w) * inv);
+      *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + (lane >> 5) * 4) = o4;
+    }
 }
 
 // ------------------------------------------------------------------ host --
@@ -756,21 +882,41 @@ int launch(const Args &args, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "frame-norm kernel launch failed: %s", hipGetErrorString(e));
   }
-  // With tickets: 1/8 more workgroups than items, so that the fastest XCD
-  // can take over up to that share of the others' items.
-  const int64_t grid = args.tickets ? args.n_wg + args.n_wg / 8 + kNumXcd : args.n_wg;
+  // With tickets: one workgroup per ticket (items, plus one more per split
+  // item), and 1/8 more, so that the fastest XCD can take over up to that
+  // share of the others' items.
+  const int64_t grid =
+      args.tickets ? args.n_wg + (int64_t)kNumXcd * args.split_cap + args.n_wg / 8 + kNumXcd : args.n_wg;
   hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (args.tickets && args.split_cap > 0) {
+    hipLaunchKernelGGL((lvsa_combine<D, NW>), dim3(kNumXcd * args.split_cap), dim3(NW * 64), 0, stream, args);
+    e = hipGetLastError();
+    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+  }
   return lvsa::ok();
 }
 
 // Workspace: the frame-norm table (B·H·T float pairs), then, at the next
-// 256-byte boundary, the 8 ticket counters (256 bytes).
+// 256-byte boundary, the 8 ticket counters (256 bytes), then the partial
+// records of the split items (8·split_cap slots × 2 halves × NW waves × 64
+// lanes × kPartialFloats(D) floats).
+constexpr int kSplitPerXcd = 96;  // items per XCD range run as two halves, at most
 int64_t norms_bytes_for(int64_t B, int64_t H, int64_t T) {
   return ((B * H * T * 2 * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
-int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t T) { return norms_bytes_for(B, H, T) + 256; }
+int64_t items_for(int64_t B, int64_t H, int64_t N, int64_t T) {
+  const int64_t P = N / T, BM = LVSA_NW * 32;
+  return B * H * T * ((P + BM - 1) / BM);
+}
+// At most a quarter of every XCD range is split.
+int32_t split_cap_for(int64_t items) { return (int32_t)std::min<int64_t>(kSplitPerXcd, items / (4 * kNumXcd)); }
+int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T) {
+  const int64_t partial =
+      (int64_t)kNumXcd * split_cap_for(items_for(B, H, N, T)) * 2 * LVSA_NW * 64 * kPartialFloats((int)D) * 4;
+  return norms_bytes_for(B, H, T) + 256 + partial;
+}
 
 int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
                    const int32_t *row_ptr_dev, const int32_t *col_idx_dev, int32_t T, int32_t nnz,
@@ -798,7 +944,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
     if ((bits & 0x7f800000u) == 0x7f800000u) return lvsa::fail(LVSA_ERR_ARG, "scale is not finite");
   }
   if (use_ws) {
-    const int64_t need = workspace_bytes_for(q->B, q->H, T);
+    const int64_t need = workspace_bytes_for(q->B, q->H, q->N, q->D, T);
     if (!workspace) return lvsa::fail(LVSA_ERR_ARG, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) % 4) return lvsa::fail(LVSA_ERR_ARG, "workspace not 4-byte aligned");
     if (workspace_bytes < need)
@@ -844,6 +990,9 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   a.fnorm = use_ws ? static_cast<const float *>(workspace) : nullptr;
   a.tickets = use_ws ? reinterpret_cast<int *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T))
                      : nullptr;
+  a.partial = use_ws ? reinterpret_cast<float *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T) + 256)
+                     : nullptr;
+  a.split_cap = use_ws ? split_cap_for(n_wg) : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) return launch<128, NW>(a, s);
@@ -859,11 +1008,15 @@ extern "C" int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const 
   return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, nullptr, 0, false, stream);
 }
 
-extern "C" int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes) {
+extern "C" int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t T,
+                                              int64_t *bytes) {
   if (!bytes) return lvsa::fail(LVSA_ERR_ARG, "bytes is NULL");
-  if (B < 1 || H < 1 || T < 1) return lvsa::fail(LVSA_ERR_ARG, "B, H and T must be >= 1");
-  if (B * H > (int64_t{1} << 40) / T) return lvsa::fail(LVSA_ERR_ARG, "B*H*T too large");
-  *bytes = workspace_bytes_for(B, H, T);
+  if (B < 1 || H < 1 || T < 1 || N < 1) return lvsa::fail(LVSA_ERR_ARG, "B, H, N and T must be >= 1");
+  if (D != 64 && D != 128) return lvsa::fail(LVSA_ERR_SHAPE, "D=%lld, supported 64 and 128", (long long)D);
+  if (N % T) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld is not a multiple of T=%d", (long long)N, T);
+  if (N > INT32_MAX / 2 || B * H > (int64_t{1} << 40) / N)
+    return lvsa::fail(LVSA_ERR_ARG, "B*H*N too large");
+  *bytes = workspace_bytes_for(B, H, N, D, T);
   return lvsa::ok();
 }
 

@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define LVSA_ABI_VERSION 1
+#define LVSA_ABI_VERSION 2
 
 /* Status codes. */
 #define LVSA_OK            0
@@ -194,10 +194,13 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
                    void *stream);
 
-/* Bytes of device workspace lvsa_attention_ws needs for B, H and T: two
- * floats per (b, h, frame), rounded up to 256, plus 256 bytes of work
- * counters.  Errors: LVSA_ERR_ARG. */
-int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *bytes);
+/* Bytes of device workspace lvsa_attention_ws needs for tensors of B, H, N
+ * tokens and head size D split into T frames: two floats per (b, h, frame)
+ * rounded up to 256, 256 bytes of work counters, and room for the partial
+ * results of the items that run as two halves (about 107 MB at D = 128
+ * once there are at least 3,072 query tiles; none below 32).
+ * Errors: LVSA_ERR_ARG, LVSA_ERR_SHAPE (D not 64/128, N % T != 0). */
+int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t T, int64_t *bytes);
 
 /* lvsa_attention with a caller-provided device workspace, used to drop the
  * online softmax's running maximum where that is safe.
@@ -217,7 +220,10 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int32_t T, int64_t *byt
  *
  * The workspace also holds one work counter per XCD: workgroups take their
  * (b, h, frame, query tile) items from counters instead of a fixed split,
- * so that faster XCDs take over items of slower ones.  Which workgroup
+ * so that faster XCDs take over items of slower ones; and the last items of
+ * each XCD's share run as two halves of their CSR row, whose partial
+ * results a second kernel merges (shorter items at the end of the launch,
+ * where the last workgroups finish at different times).  Which workgroup
  * computes an item does not change its result: outputs are bitwise
  * reproducible from call to call.
  *

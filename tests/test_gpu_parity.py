@@ -270,7 +270,8 @@ def test_deterministic(gpu):
 
 def workspace_for(q, T):
     B, H = q.shape[0], q.shape[1]
-    return torch.empty(L.lvsa_attention_workspace_bytes(B, H, T), dtype=torch.uint8, device=q.device)
+    return torch.empty(L.lvsa_attention_workspace_bytes(B, H, q.shape[2], q.shape[3], T), dtype=torch.uint8,
+                       device=q.device)
 
 
 @pytest.mark.parametrize("flags", [L.LVSA_ROT_MOD_TPER, L.LVSA_FIXED_GRID, L.LVSA_WINDOW_ONLY])
@@ -311,11 +312,13 @@ def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(g
     # path).  Keys shifted by a large common vector make |q|·max|k| far above
     # the true scores: every wave must fall back, giving the running-max
     # path's output bit for bit.  Mixed: large-norm query rows in some waves.
+    # One head: 18 work items, too few for the workspace path to run any item
+    # as two halves (which would round differently from lvsa_attention).
     T, P, d, C, W = 9, 200, 128, 4, 2
     say("workspace reference choice", (T, P, d, C, W))
-    q = make_random((1, 2, T * P, d), 901)
-    k = make_random((1, 2, T * P, d), 902)
-    v = make_random((1, 2, T * P, d), 903)
+    q = make_random((1, 1, T * P, d), 901)
+    k = make_random((1, 1, T * P, d), 902)
+    v = make_random((1, 1, T * P, d), 903)
     m = L.lvsa_build_mask(T, C, W, 1).to(gpu)
     rows = om.key_frames(T, C, W, 1)
     qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
@@ -339,7 +342,7 @@ def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(g
     a = L.lvsa_attention(qmd, kd, vd, m, workspace=ws)
     torch.cuda.synchronize()
     toks = [0, 250, 299, 300, 320, 339, 340, 1000, T * P - 1]
-    assert_close(a[0, 1, toks], oa.block_attention_rows(q_mixed, k, v, rows, 0, 1, toks), "mixed waves")
+    assert_close(a[0, 0, toks], oa.block_attention_rows(q_mixed, k, v, rows, 0, 0, toks), "mixed waves")
     # Values so large (2^100) that unnormalised probabilities up to 2^R
     # could overflow the fp32 accumulators: the value-magnitude guard sends
     # every wave whose row lists frame 4 to the running max (bit-identical),
@@ -380,6 +383,47 @@ def test_workspace_full_size_sampled(gpu, name, steps):
         ref = torch.stack([oa.block_attention_rows(*host[h], rows, 0, 0, toks) for h in heads])
         assert_close(got, ref, f"ws {name} step {s}")
         assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("tail_rows", [([5], []), ([3, 1, 3, 4], [2, 2, 0, 7, 6])], ids=["single-and-empty", "malformed"])
+def test_workspace_split_items_merge_their_halves(gpu, tail_rows):
+    # With a workspace, the last items of each XCD range run as two halves of
+    # their CSR row, merged afterwards.  Here 8 heads x 8 frames x 2 query
+    # tiles = 128 items, 16 per range: each range is one head, and its last 4
+    # items (frames 6 and 7) are split.  Those rows are a single entry (the
+    # first half sees no key), an empty row (neither does), or malformed
+    # rows whose skipped entries straddle the split point.  Every output row
+    # must match the oracle on the kept entries; empty rows give zeros.
+    B, H, T, P, d = 1, 8, 8, 150, 64
+    say("workspace split halves", (B, H, T, P, d), tail_rows)
+    q = make_random((B, H, T * P, d), 411)
+    k = make_random((B, H, T * P, d), 412)
+    v = make_random((B, H, T * P, d), 413)
+    raw = [[0, 1], [0, 1, 2], [1, 2, 3], [2, 3, 4], [3, 4, 5], [4, 5, 6], tail_rows[0], tail_rows[1]]
+    rows = [kept_entries(r, T) for r in raw]
+    rp = [0]
+    ci = []
+    for r in raw:
+        ci += r
+        rp.append(len(ci))
+    m = L.Mask(torch.tensor(rp, dtype=torch.int32), torch.tensor(ci, dtype=torch.int32),
+               T, 0, 0, 0, 0, len(ci)).to(gpu)
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    ws = workspace_for(qd, T)
+    o = torch.full_like(qd, float("nan"))
+    L.lvsa_attention(qd, kd, vd, m, out=o, workspace=ws)
+    o_exact = L.lvsa_attention(qd, kd, vd, m)
+    torch.cuda.synchronize()
+    o, o_exact = o.cpu(), o_exact.cpu()
+    assert torch.isfinite(o.float()).all()
+    for t, r in enumerate(rows):
+        sl = slice(t * P, (t + 1) * P)
+        if not r:
+            assert torch.count_nonzero(o[:, :, sl]) == 0
+        else:
+            ref = oa.block_attention(q, k, v, [r if i == t else [i] for i in range(T)])
+            assert_close(o[:, :, sl], ref[:, :, sl], f"row {t}")
+            assert_close(o[:, :, sl], o_exact[:, :, sl].double(), f"row {t} vs lvsa_attention")
 
 
 def test_workspace_results_are_reproducible_and_cover_every_row(gpu):

@@ -56,7 +56,7 @@ def test_graph_replay_of_the_step_sequence(gpu, with_workspace):
     _, (qd, kd, vd) = _inputs(gpu, B, H, T, P, d, 801)
     n = 8
     ms = L.lvsa_build_mask_steps(T, C, W, 0, n).to(gpu)
-    ws = (torch.empty(L.lvsa_attention_workspace_bytes(B, H, T), dtype=torch.uint8, device=gpu)
+    ws = (torch.empty(L.lvsa_attention_workspace_bytes(B, H, T * P, d, T), dtype=torch.uint8, device=gpu)
           if with_workspace else None)
     outs = [torch.empty_like(qd) for _ in range(n)]
     for i in range(n):
