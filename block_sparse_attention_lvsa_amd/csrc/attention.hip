@@ -31,8 +31,8 @@
 //   Online softmax in the log2 domain with a lazily updated running max
 //   (rescale only when the tile max exceeds it by more than 2^8, so exp2
 //   arguments stay <= 8 and fp32 cannot overflow); or, given per-frame
-//   key and value norms, no reference at all where a Cauchy-Schwarz bound
-//   keeps every exponent within ±64 (P = 2^S straight from the MFMA).
+//   key norms, a fixed per-row reference from a Cauchy-Schwarz bound,
+//   subtracted by starting the Q·Kᵀ chain from it.
 //   Oᵀ(d × 32 queries) += Vᵀ · Pᵀ         P (bf16) comes straight from the Sᵀ
 //                                         accumulator registers; the Vᵀ
 //                                         operand is built by transposing
@@ -89,14 +89,11 @@ typedef uint16_t u16;
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
-// Largest bound R on |score·scale·log2e| for which a wave exponentiates its
-// scores against a fixed reference of 0: every probability then lies in
-// [2^-R, 2^R], inside the normal range of fp32 and bf16 (2^±126), and the
-// largest of a row is at least 2^-R.
-constexpr float kMaxExp = 64.0f;
-// ... provided n_keys · 2^R · max|v| stays below this, so that neither the
-// row sum nor the P·V accumulators can overflow fp32.
-constexpr float kMaxAcc = 0x1p120f;
+// Largest log2 gap a fixed softmax reference may leave below a row's true
+// maximum: with the reference at most 96 above it (its bound, below), the
+// largest probability of the row stays >= 2^-96, far inside the normal
+// range of fp32 and bf16 (2^-126).
+constexpr float kMaxRefGap = 96.0f;
 
 struct Args {
   const u16 *q, *k, *v;
@@ -106,10 +103,9 @@ struct Args {
   const int32_t *row_ptr, *col_idx;
   int32_t nnz, T, P, H, q_tiles, n_wg;
   float scale_log2;  // softmax scale × log2(e)
-  // Per (b, h, frame), [B·H·T][2]: the largest key norm max_j |k_j| and the
-  // largest value magnitude max |v_jd|; or null: then every wave uses the
-  // running-max softmax.
-  const float *fnorm;
+  // Per (b, h, frame), [B·H·T]: the largest key norm max_j |k_j|; or null:
+  // then every wave uses the running-max softmax.
+  const float *knorm;
   // Per-XCD work-item counters, zeroed before the launch, or null: then
   // workgroup i runs the (i mod 8)-th XCD's (i div 8)-th item.
   int *tickets;
@@ -229,7 +225,8 @@ struct Block {
   float scale_log2;
   bf16x8_t qf[D / 16];         // the wave's Q rows, B-operand layout
   f32x16_t oacc[D / 32];       // Oᵀ accumulators (dims × 32 queries)
-  float m_run;                 // running row max, log2 domain (lazily raised)
+  float m_run;                 // running row max, log2 domain (lazily raised), or the fixed reference
+  f32x16_t bias;               // with a fixed reference R: -R, the Q·Kᵀ chain's initial accumulator
   float l_run;                 // this lane's partial row sum
   int32_t kro[D / 16];         // LDS byte offsets of this lane's K operands
   int32_t vro[D / 32];         // LDS byte offsets of this lane's V source rows
@@ -282,11 +279,14 @@ struct Block {
   }
 
   // Sᵀ (keys × 32 queries) of the K tile in buffer KBUF.
-  template <int KBUF>
+  // With a fixed reference (FIXED) the chain starts from -R instead of 0, so
+  // the accumulators come out as S·scale·log2e - R with no extra instruction
+  // (the wave's Q rows are then pre-scaled by scale·log2e).
+  template <int KBUF, bool FIXED>
   __device__ __forceinline__ void qk(f32x16_t (&sc)[C::KB]) const {
     const char *Kb = lds + kTileOffK(KBUF);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) sc[kb] = f32x16_t{};
+    for (int kb = 0; kb < C::KB; ++kb) sc[kb] = FIXED ? bias : f32x16_t{};
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
@@ -351,10 +351,9 @@ struct Block {
 
   // Probabilities of a tile, rounded to bf16, in the MFMA B-operand order of
   // the P·V product: P = 2^(S·scale·log2e − m_run) once the tile's maximum
-  // has been folded into m_run, or, with a fixed reference (FIXED), P = 2^S
-  // straight from the accumulators (the wave's Q rows are then pre-scaled by
-  // scale·log2e).  The row sum takes the same rounded values, so the
-  // normalised weights sum to one.
+  // has been folded into m_run, or, with a fixed reference (FIXED), straight
+  // from the accumulators, which already hold S·scale·log2e − R.  The row
+  // sum takes the same rounded values, so the normalised weights sum to one.
   template <bool FIXED>
   __device__ __forceinline__ void probs(const f32x16_t (&sc)[C::KB], bf16x8_t (&pb)[2 * C::KB]) {
     const float neg_m = -m_run;
@@ -399,7 +398,7 @@ struct Block {
   __device__ __forceinline__ void tile(int kv) {
     f32x16_t sc[C::KB];
     bf16x8_t pb[2 * C::KB];
-    qk<BUF>(sc);
+    qk<BUF, FIXED>(sc);
     mask_tail(sc, kv);
     if constexpr (!FIXED) fold_max(sc);
     probs<FIXED>(sc, pb);
@@ -558,24 +557,22 @@ void lvsa_attn_fwd(Args a) {
     }
   }
 
-  // ---- softmax reference.  Without a frame-norm table: the running max,
+  // ---- softmax reference.  Without a key-norm table: the running max,
   // raised lazily.  With one: by Cauchy-Schwarz every score of query i lies
-  // within ±|q_i|·K, K the largest key norm over the row's frames.  If
-  // R_i = scale·log2e·|q_i|·K·(1 + 2^-8) (the factor covers the rounding of
-  // the fp32 norms and of the MFMA dot products) is at most kMaxExp on every
-  // lane, and n_keys·2^R·max|v| below kMaxAcc, the wave pre-scales its Q rows
-  // by scale·log2e (rounded to bf16) and takes P = 2^S with no reference at
-  // all: no running max, no rescale, no subtraction.
+  // within ±|q_i|·K, K the largest key norm over the row's frames, so
+  // R_i = scale·log2e·|q_i|·K·(1 + 2^-8) bounds every exponent (the factor
+  // covers the rounding of the fp32 norms and of the MFMA dot products).  A
+  // wave whose lanes all have 2·R_i <= kMaxRefGap (the bound cannot sit more
+  // than 2·R_i above a row's true maximum) takes R_i as a fixed reference:
+  // no running max, no rescale, and the subtraction is folded into the
+  // Q·Kᵀ chain's initial accumulator.  Other waves keep the running max.
   bool fixed = false;
-  if (a.fnorm) {
-    const const_f32p fn = (const_f32p)(a.fnorm + (int64_t)bh * a.T * 2);
-    float kn = 0.f, vn = 0.f;
+  if (a.knorm) {
+    const const_f32p fn = (const_f32p)(a.knorm + (int64_t)bh * a.T);
+    float kn = 0.f;
     for (int32_t e = rb; e < re; ++e) {  // the whole row, so both halves decide alike
       const int32_t f = it.cols[e];
-      if (f >= 0 && f < a.T) {
-        kn = fmaxf(kn, fn[2 * f]);
-        vn = fmaxf(vn, fn[2 * f + 1]);
-      }
+      if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
     }
     float ss = 0.f;  // |q'_i|^2 of the scaled, rounded rows
 #pragma unroll
@@ -586,12 +583,12 @@ void lvsa_attn_fwd(Args a) {
         ss = __builtin_fmaf(x, x, ss);
       }
     ss = swap_halves_sum(ss);  // each lane half holds half of the row
-    const float r_exp = __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
-    const float acc = __builtin_amdgcn_exp2f(fminf(r_exp, kMaxExp)) * (float)n_tiles * (float)C::BN * vn;
-    const bool ok = r_exp <= kMaxExp && acc < kMaxAcc;
-    fixed = __builtin_amdgcn_ballot_w64(!ok) == 0;
+    const float r_ref = __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
+    fixed = __builtin_amdgcn_ballot_w64(!(2.0f * r_ref <= kMaxRefGap)) == 0;
     if (fixed) {
-      blk.m_run = 0.f;  // the reference is 0 (a partial record carries it)
+      blk.m_run = r_ref;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) blk.bias[e] = -r_ref;
 #pragma unroll
       for (int dc = 0; dc < D / 16; ++dc)
 #pragma unroll
@@ -690,57 +687,41 @@ void lvsa_attn_fwd(Args a) {
   }
 }
 
-// Norms of one (b, h, frame): one workgroup per frame streams its P key and
-// value rows once (16 bytes per lane, D/8 lanes per row) and writes
-// max_j |k_j| (from fp32 sums of squares of the bf16 values) and max |v_jd|
-// to fnorm[((b·H + h)·T + t)·2 + {0, 1}].  Workgroup 0 also zeroes the
-// attention kernel's 8 ticket counters.
+// Largest key norm of one (b, h, frame): one workgroup per frame streams its
+// P key rows once (16 bytes per lane, D/8 lanes per row) and writes
+// max_j |k_j| (from fp32 sums of squares of the bf16 values) to
+// knorm[(b·H + h)·T + t].  Workgroup 0 also zeroes the attention kernel's 8
+// ticket counters.
 template <int D>
-__global__ __launch_bounds__(256) void lvsa_frame_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
-                                                        const u16 *v, int64_t v_sb, int64_t v_sh, int32_t v_sn,
-                                                        int32_t H, int32_t T, int32_t P, float *fnorm,
-                                                        int *tickets) {
+__global__ __launch_bounds__(256) void lvsa_key_norms(const u16 *k, int64_t k_sb, int64_t k_sh, int32_t k_sn,
+                                                      int32_t H, int32_t T, int32_t P, float *knorm, int *tickets) {
   if (blockIdx.x == 0 && threadIdx.x < kNumXcd)  // for the attention launch that follows
     __hip_atomic_store(tickets + threadIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int LPR = D / 8;          // lanes per key row
   constexpr int RPI = 256 / LPR;      // rows per workgroup iteration
   const int item = blockIdx.x;        // (b·H + h)·T + t
   const int t = item % T;
   const int bh = item / T;
   const int h = bh % H;
   const int b = bh / H;
-  const u16 *kb = k + (int64_t)b * k_sb + (int64_t)h * k_sh + (int64_t)t * P * k_sn;
-  const u16 *vb = v + (int64_t)b * v_sb + (int64_t)h * v_sh + (int64_t)t * P * v_sn;
+  const u16 *base = k + (int64_t)b * k_sb + (int64_t)h * k_sh + (int64_t)t * P * k_sn;
   const int col = (threadIdx.x % LPR) * 8;
-  float kbest = 0.f, vbest = 0.f;
+  float best = 0.f;
   for (int r = threadIdx.x / LPR; r < P; r += RPI) {
-    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(kb + (int64_t)r * k_sn + col);
-    const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(vb + (int64_t)r * v_sn + col);
+    const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(base + (int64_t)r * k_sn + col);
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ss = __builtin_fmaf((float)x[e], (float)x[e], ss);
-      vbest = fmaxf(vbest, __builtin_fabsf((float)y[e]));
-    }
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf((float)x[e], (float)x[e], ss);
 #pragma unroll
     for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);  // the row's LPR lanes
-    kbest = fmaxf(kbest, ss);
+    best = fmaxf(best, ss);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kbest = fmaxf(kbest, __shfl_xor(kbest, o));
-    vbest = fmaxf(vbest, __shfl_xor(vbest, o));
-  }
-  __shared__ float wk[4], wv[4];
-  if ((threadIdx.x & 63) == 0) {
-    wk[threadIdx.x >> 6] = kbest;
-    wv[threadIdx.x >> 6] = vbest;
-  }
+  for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    fnorm[2 * item] = __builtin_sqrtf(fmaxf(fmaxf(wk[0], wk[1]), fmaxf(wk[2], wk[3])));
-    fnorm[2 * item + 1] = fmaxf(fmaxf(wv[0], wv[1]), fmaxf(wv[2], wv[3]));
-  }
+  if (threadIdx.x == 0) knorm[item] = __builtin_sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 }
 
 // Merges the two halves of every split item: one workgroup per record slot,
@@ -874,13 +855,12 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
 
 template <int D, int NW>
 int launch(const Args &args, hipStream_t stream) {
-  if (args.fnorm) {
-    // the frame-norm table first, on the same stream
-    hipLaunchKernelGGL((lvsa_frame_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
-                       args.k_sh, args.k_sn, args.v, args.v_sb, args.v_sh, args.v_sn, args.H, args.T, args.P,
-                       const_cast<float *>(args.fnorm), args.tickets);
+  if (args.knorm) {
+    // the key-norm table first, on the same stream
+    hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
+                       args.k_sh, args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.knorm), args.tickets);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "frame-norm kernel launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "key-norm kernel launch failed: %s", hipGetErrorString(e));
   }
   // With tickets: one workgroup per ticket (items, plus one more per split
   // item), and 1/8 more, so that the fastest XCD can take over up to that
@@ -898,13 +878,13 @@ int launch(const Args &args, hipStream_t stream) {
   return lvsa::ok();
 }
 
-// Workspace: the frame-norm table (B·H·T float pairs), then, at the next
+// Workspace: the key-norm table (B·H·T floats), then, at the next
 // 256-byte boundary, the 8 ticket counters (256 bytes), then the partial
 // records of the split items (8·split_cap slots × 2 halves × NW waves × 64
 // lanes × kPartialFloats(D) floats).
 constexpr int kSplitPerXcd = 96;  // items per XCD range run as two halves, at most
 int64_t norms_bytes_for(int64_t B, int64_t H, int64_t T) {
-  return ((B * H * T * 2 * (int64_t)sizeof(float) + 255) / 256) * 256;
+  return ((B * H * T * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
 int64_t items_for(int64_t B, int64_t H, int64_t N, int64_t T) {
   const int64_t P = N / T, BM = LVSA_NW * 32;
@@ -987,7 +967,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   a.n_wg = (int32_t)n_wg;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  a.fnorm = use_ws ? static_cast<const float *>(workspace) : nullptr;
+  a.knorm = use_ws ? static_cast<const float *>(workspace) : nullptr;
   a.tickets = use_ws ? reinterpret_cast<int *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T))
                      : nullptr;
   a.partial = use_ws ? reinterpret_cast<float *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T) + 256)

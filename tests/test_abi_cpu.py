@@ -185,16 +185,16 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
 
 
 def test_workspace_bytes():
-    # frame norms: B*H*T frames x 2 floats, rounded up to 256 bytes; 256 bytes
+    # key norms: B*H*T frames x 1 float, rounded up to 256 bytes; 256 bytes
     # of counters; then the partial records of the split items: 8 XCD ranges
     # x min(96, items / 32) items x 2 halves x 4 waves x 64 lanes x (D/2 + 4)
     # floats, items = B*H*T*ceil(P/128)
     rec = 8 * 96 * 2 * 4 * 64 * 68 * 4
-    assert L.lvsa_attention_workspace_bytes(1, 12, 121 * 1560, 128, 121) == 11776 + 256 + rec
-    assert L.lvsa_attention_workspace_bytes(2, 40, 121 * 1560, 128, 121) == 77568 + 256 + rec
+    assert L.lvsa_attention_workspace_bytes(1, 12, 121 * 1560, 128, 121) == 5888 + 256 + rec
+    assert L.lvsa_attention_workspace_bytes(2, 40, 121 * 1560, 128, 121) == 38912 + 256 + rec
     assert L.lvsa_attention_workspace_bytes(1, 2, 8 * 64, 64, 8) == 512  # 16 items: nothing split
     # 1 x 4 x 40 frames x 1 tile = 160 items: 5 per XCD range, (D/2 + 4) = 36 floats
-    assert L.lvsa_attention_workspace_bytes(1, 4, 40 * 100, 64, 40) == 1280 + 256 + 8 * 5 * 2 * 4 * 64 * 36 * 4
+    assert L.lvsa_attention_workspace_bytes(1, 4, 40 * 100, 64, 40) == 768 + 256 + 8 * 5 * 2 * 4 * 64 * 36 * 4
     lib = L.library()
     n = ctypes.c_int64(0)
     assert lib.lvsa_attention_workspace_bytes(0, 2, 512, 64, 8, ctypes.byref(n)) == L.LVSA_ERR_ARG
@@ -215,7 +215,7 @@ def test_workspace_errors_are_reported_before_any_device_work():
     sz = 2 * 512 * 64 * 2
     q, k, v, o = (_rec(base + i * sz) for i in range(4))
     ws = base + 8 * sz
-    need = L.lvsa_attention_workspace_bytes(1, 2, 512, 64, 8)  # 2·8·2 floats -> 256 bytes, + 256 of counters
+    need = L.lvsa_attention_workspace_bytes(1, 2, 512, 64, 8)  # 2·8 floats -> 256 bytes, + 256 of counters
     assert need == 512
     assert _attn_ws(q, k, v, o, 0, need) == L.LVSA_ERR_ARG                # NULL
     assert "NULL" in L.lvsa_last_error()

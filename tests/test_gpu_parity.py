@@ -265,7 +265,7 @@ def test_deterministic(gpu):
     assert torch.equal(a, b)
 
 
-# ------------------------ the workspace path (no softmax reference) --
+# ------------------------ the workspace path (fixed softmax reference) --
 
 
 def workspace_for(q, T):
@@ -306,9 +306,9 @@ def test_workspace_mid_size(gpu, case):
         assert_close(o, o_exact.double().cpu(), f"ws vs exact path, step {s}")
 
 
-def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(gpu):
+def test_workspace_takes_a_fixed_reference_and_falls_back_on_large_norms(gpu):
     # Unit-variance d=128 inputs: every wave's bound is close enough, so the
-    # reference-free path is used (outputs round differently from the running-max
+    # fixed reference is used (outputs round differently from the running-max
     # path).  Keys shifted by a large common vector make |q|·max|k| far above
     # the true scores: every wave must fall back, giving the running-max
     # path's output bit for bit.  Mixed: large-norm query rows in some waves.
@@ -326,8 +326,8 @@ def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(g
     a = L.lvsa_attention(qd, kd, vd, m, workspace=ws)
     b = L.lvsa_attention(qd, kd, vd, m)
     torch.cuda.synchronize()
-    assert not torch.equal(a, b)  # the reference-free path was used
-    assert_close(a, oa.block_attention(q, k, v, rows), "no reference")
+    assert not torch.equal(a, b)  # the fixed reference was used
+    assert_close(a, oa.block_attention(q, k, v, rows), "fixed reference")
     u = q.float().mean(dim=(0, 1, 2))
     k_far = (k.float() + u / u.norm() * 400.0).to(torch.bfloat16)
     a = L.lvsa_attention(qd, k_far.to(gpu), vd, m, workspace=ws)
@@ -343,20 +343,13 @@ def test_workspace_drops_the_reference_and_falls_back_on_large_norms_or_values(g
     torch.cuda.synchronize()
     toks = [0, 250, 299, 300, 320, 339, 340, 1000, T * P - 1]
     assert_close(a[0, 0, toks], oa.block_attention_rows(q_mixed, k, v, rows, 0, 0, toks), "mixed waves")
-    # Values so large (2^100) that unnormalised probabilities up to 2^R
-    # could overflow the fp32 accumulators: the value-magnitude guard sends
-    # every wave whose row lists frame 4 to the running max (bit-identical),
-    # the rest keep the fixed path.
+    # Values of 2^100 in one frame: with probabilities at most 1 on either
+    # path, the accumulators stay finite, and the output matches the oracle.
     v_big = v.clone()
     v_big[:, :, 4 * P:5 * P] *= 2.0 ** 100
     vbd = v_big.to(gpu)
     a = L.lvsa_attention(qd, kd, vbd, m, workspace=ws)
-    b = L.lvsa_attention(qd, kd, vbd, m)
     torch.cuda.synchronize()
-    uses4 = torch.tensor([4 in r for r in rows]).repeat_interleave(P)
-    assert uses4.any() and not uses4.all()
-    assert torch.equal(a[:, :, uses4], b[:, :, uses4])
-    assert not torch.equal(a[:, :, ~uses4], b[:, :, ~uses4])
     assert torch.isfinite(a.float()).all()
     toks = [0, 4 * P, 4 * P + 150, T * P - 1]
     assert_close(a[0, 0, toks], oa.block_attention_rows(q, k, v_big, rows, 0, 0, toks), "large values")
