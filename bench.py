@@ -3,8 +3,8 @@
 One step = one denoising step of the attention hot path over the whole
 workload: build the step's CSR mask on the host (C++), copy it to the device,
 run the frame-block-sparse attention on [B, H, T·P, d] bf16 (by default
-through lvsa_attention_ws: a frame-norm pass, then the attention kernel
-without a softmax reference where the norm bound allows; --no-workspace times
+through lvsa_attention_ws: a key-norm pass, then the attention kernel
+with a fixed softmax reference where the norm bound allows; --no-workspace times
 lvsa_attention, the running-max path).  The
 default workload is the Wan-2.1-1.3B-shaped 6× horizon: B=1, H=12, d=128,
 T=121 latent frames × 1560 tokens (480×832 video), C=21, W=9, anchors
@@ -169,8 +169,8 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
     d_ci = torch.empty(nnz, dtype=torch.int32, device=dev)
     info = L.LvsaMaskInfo()
     recs = [L._tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
-    # With a workspace the call is lvsa_attention_ws: a frame-norm pass, then
-    # the attention without a softmax reference where the bound allows.
+    # With a workspace the call is lvsa_attention_ws: a key-norm pass, then
+    # the attention with a fixed softmax reference where the bound allows.
     ws_bytes = L.lvsa_attention_workspace_bytes(w.B, w.H, T * w.P, w.D, T) if workspace else 0
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
@@ -237,7 +237,7 @@ def run_workload(w, steps, warmup, dense, calib_copy=False, keep_inputs=False, m
         "mask_build_us_median": statistics.median(mask_times) * 1e6,
         "mask_h2d_ms_median": statistics.median(h2d),
         "flops_per_step": flops,
-        "path": "lvsa_attention_ws (frame-norm pass + no softmax reference where the bound allows)" if workspace
+        "path": "lvsa_attention_ws (key-norm pass + fixed softmax reference where the bound allows)" if workspace
                 else "lvsa_attention (running-max softmax)",
     }
     if modes:
@@ -392,7 +392,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_frame_norms<128> and lvsa_combine<128,4> in the timed call)"
+            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_key_norms<128> and lvsa_combine<128,4> in the timed call)"
                                                 if not args.no_workspace else ""),
             "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
 

@@ -195,7 +195,7 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    void *stream);
 
 /* Bytes of device workspace lvsa_attention_ws needs for tensors of B, H, N
- * tokens and head size D split into T frames: two floats per (b, h, frame)
+ * tokens and head size D split into T frames: one float per (b, h, frame)
  * rounded up to 256, 256 bytes of work counters, and room for the partial
  * results of the items that run as two halves (about 107 MB at D = 128
  * once there are at least 3,072 query tiles; none below 32).
@@ -207,16 +207,16 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, i
  *
  * Source: the same computation as lvsa_attention (gist.science explainer,
  * Technical Summary §2).  The workspace changes only the softmax's reference
- * point, which cancels in the normalisation: a first kernel writes, for every
- * (b, h, frame), the largest key norm and the largest |value| element to the
- * workspace.  By Cauchy-Schwarz, R_i = scale·log2(e)·|q_i|·(largest key norm
- * over A(t)) bounds |score·log2(e)| of query i; a wave whose 64 lanes all have
- * R_i <= 64, and whose unnormalised sums cannot overflow fp32 (keys·2^R·
- * max|v| < 2^120), exponentiates its scores with no reference at all -- no
- * running maximum, no rescaling, no subtraction (its Q rows are pre-scaled
- * by scale·log2(e) and rounded to bf16).  Other waves keep the
- * running-maximum path of lvsa_attention, bit for bit.  Results agree with
- * lvsa_attention to the same accuracy, not bit for bit.
+ * point, which cancels in the normalisation: a first kernel writes the
+ * largest key norm of every (b, h, frame) to the workspace.  By
+ * Cauchy-Schwarz, R_i = scale·log2(e)·|q_i|·(largest key norm over A(t))
+ * bounds |score·log2(e)| of query i; a wave whose 64 lanes all have
+ * 2·R_i <= 96 (every row's largest probability then >= 2^-96) takes R_i as
+ * a fixed reference -- no running maximum, no rescaling, and the subtraction
+ * folded into the Q·K^T product (its Q rows are pre-scaled by
+ * scale·log2(e) and rounded to bf16).  Other waves keep the running-maximum
+ * path of lvsa_attention, bit for bit.  Results agree with lvsa_attention
+ * to the same accuracy, not bit for bit.
  *
  * The workspace also holds one work counter per XCD: workgroups take their
  * (b, h, frame, query tile) items from counters instead of a fixed split,
@@ -229,7 +229,7 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, i
  *
  * Arguments as lvsa_attention, plus:
  *   workspace        : device memory of at least
- *                      lvsa_attention_workspace_bytes(B, H, T) bytes,
+ *                      lvsa_attention_workspace_bytes(B, H, N, D, T) bytes,
  *                      4-byte aligned, not overlapping q/k/v/out.  Owned by
  *                      the caller; overwritten by the call (stream-ordered),
  *                      so concurrent calls need separate workspaces.

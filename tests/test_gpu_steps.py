@@ -49,7 +49,7 @@ def test_prebuilt_masks_match_per_step_masks(gpu):
 
 @pytest.mark.parametrize("with_workspace", [False, True], ids=["running-max", "workspace"])
 def test_graph_replay_of_the_step_sequence(gpu, with_workspace):
-    # With a workspace each step is two kernels (frame norms, attention), both
+    # With a workspace each step is three kernels (key norms, attention, merge), all
     # captured.
     B, H, T, P, d, C, W = 1, 3, 11, 150, 128, 4, 2
     say("graph replay", (B, H, T, P, d, C, W), "workspace" if with_workspace else "")
