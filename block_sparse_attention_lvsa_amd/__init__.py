@@ -269,18 +269,22 @@ def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None,
         if t.device != q.device or t.dtype != torch.int32 or not t.is_contiguous():
             raise LvsaValueError(LVSA_ERR_ARG, f"mask.{name}: need contiguous int32 on {q.device}")
     rq, rk, rv, ro = (_tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.device != q.device:
+            raise LvsaValueError(LVSA_ERR_ARG, f"{name}: on {t.device}, q on {q.device}")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     args = (ctypes.byref(rq), ctypes.byref(rk), ctypes.byref(rv),
             ctypes.c_void_p(mask.row_ptr.data_ptr()), ctypes.c_void_p(mask.col_idx.data_ptr()),
             mask.T, mask.col_idx.numel(), ctypes.byref(ro), 0.0 if scale is None else float(scale))
-    if workspace is None:
-        _check(library().lvsa_attention(*args, ctypes.c_void_p(sp)))
-    else:
-        if not workspace.is_cuda or workspace.device != q.device:
-            raise LvsaValueError(LVSA_ERR_ARG, f"workspace: need a device tensor on {q.device}")
-        nbytes = workspace.numel() * workspace.element_size()
-        _check(library().lvsa_attention_ws(*args, ctypes.c_void_p(workspace.data_ptr()), nbytes,
-                                           ctypes.c_void_p(sp)))
+    if workspace is not None and (not workspace.is_cuda or workspace.device != q.device):
+        raise LvsaValueError(LVSA_ERR_ARG, f"workspace: need a device tensor on {q.device}")
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        if workspace is None:
+            _check(library().lvsa_attention(*args, ctypes.c_void_p(sp)))
+        else:
+            nbytes = workspace.numel() * workspace.element_size()
+            _check(library().lvsa_attention_ws(*args, ctypes.c_void_p(workspace.data_ptr()), nbytes,
+                                               ctypes.c_void_p(sp)))
     return out

@@ -926,7 +926,8 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   if (use_ws) {
     const int64_t need = workspace_bytes_for(q->B, q->H, q->N, q->D, T);
     if (!workspace) return lvsa::fail(LVSA_ERR_ARG, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) % 4) return lvsa::fail(LVSA_ERR_ARG, "workspace not 4-byte aligned");
+    // the partial records are written and read 16 bytes at a time
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return lvsa::fail(LVSA_ERR_ARG, "workspace not 16-byte aligned");
     if (workspace_bytes < need)
       return lvsa::fail(LVSA_ERR_CAPACITY, "workspace of %lld bytes < required %lld", (long long)workspace_bytes,
                         (long long)need);

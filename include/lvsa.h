@@ -186,6 +186,7 @@ int lvsa_validate_mask(int32_t T, const int32_t *row_ptr, const int32_t *col_idx
  *   nnz          : length of col_idx_dev.
  *   scale        : softmax scale; <= 0 selects 1/sqrt(D).
  *   stream       : hipStream_t to launch on (NULL = default stream).
+ * Tensors, mask arrays and stream belong to the current HIP device.
  * The call is asynchronous on `stream`.  Argument errors are reported
  * synchronously and launch nothing.  Errors: LVSA_ERR_ARG, LVSA_ERR_SHAPE,
  * LVSA_ERR_DTYPE, LVSA_ERR_HIP (no gfx950 device current, launch failure). */
@@ -230,7 +231,7 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, i
  * Arguments as lvsa_attention, plus:
  *   workspace        : device memory of at least
  *                      lvsa_attention_workspace_bytes(B, H, N, D, T) bytes,
- *                      4-byte aligned, not overlapping q/k/v/out.  Owned by
+ *                      16-byte aligned, not overlapping q/k/v/out.  Owned by
  *                      the caller; overwritten by the call (stream-ordered),
  *                      so concurrent calls need separate workspaces.
  *   workspace_bytes  : its size.

@@ -220,6 +220,8 @@ def test_workspace_errors_are_reported_before_any_device_work():
     assert _attn_ws(q, k, v, o, 0, need) == L.LVSA_ERR_ARG                # NULL
     assert "NULL" in L.lvsa_last_error()
     assert _attn_ws(q, k, v, o, ws + 2, need) == L.LVSA_ERR_ARG           # misaligned
+    assert _attn_ws(q, k, v, o, ws + 8, need) == L.LVSA_ERR_ARG           # 16-byte records
+    assert "16-byte" in L.lvsa_last_error()
     assert _attn_ws(q, k, v, o, ws, need - 1) == L.LVSA_ERR_CAPACITY      # too small
     assert _attn_ws(q, k, v, o, base + 16, need) == L.LVSA_ERR_ARG        # inside q
     assert "overlaps" in L.lvsa_last_error()
