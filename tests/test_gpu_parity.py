@@ -488,3 +488,30 @@ def test_full_size_sampled(gpu, name, steps, flag_list):
                 got.append(o[0, h, toks].cpu())
             assert_close(torch.stack(got), torch.stack(ref), f"{name} step {s} flags {flags}")
             assert torch.isfinite(o).all()
+
+
+def test_dense_mask_at_full_size_sampled(gpu):
+    # The comparator the benchmark times: the 121-frame workload with C = T,
+    # so every query frame lists all 121 frames (one run of 188,760 keys,
+    # 5,899 key tiles per workgroup), through both entry points.
+    w = WORKLOADS["wan13b_6x"]
+    say("dense full", w)
+    q, k, v = make_qkv(w, device=gpu)
+    m = L.lvsa_build_mask(w.T, w.T, 1, 0)
+    rows = om.key_frames(w.T, w.T, 1, 0)
+    assert m.nnz == w.T * w.T and all(r == list(range(w.T)) for r in rows)
+    md = m.to(gpu)
+    a = L.lvsa_attention(q, k, v, md)
+    b = L.lvsa_attention(q, k, v, md, workspace=workspace_for(q, w.T))
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all() and torch.isfinite(b).all()
+    rnd = random.Random(w.seed + 29)
+    h = w.H - 1
+    qh, kh, vh = (x[:, h:h + 1].cpu() for x in (q, k, v))
+    for t in (0, w.T // 2, w.T - 1):  # one frame at a time bounds the oracle's float64 K/V copies
+        toks = {t * w.P + p for p in (0, 127, 128, w.P - 25, w.P - 24, w.P - 1)}
+        toks |= {t * w.P + rnd.randrange(w.P) for _ in range(3)}
+        toks = sorted(toks)
+        ref = oa.block_attention_rows(qh, kh, vh, rows, 0, 0, toks)
+        assert_close(a[0, h, toks].cpu(), ref, f"dense, running max, frame {t}")
+        assert_close(b[0, h, toks].cpu(), ref, f"dense, workspace, frame {t}")
