@@ -235,6 +235,9 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, i
  *                      the caller; overwritten by the call (stream-ordered),
  *                      so concurrent calls need separate workspaces.
  *   workspace_bytes  : its size.
+ * After the call (stream-ordered), the workspace's first B·H·T floats hold
+ * the largest key norm of every (b, h, frame) at index (b·H + h)·T + t,
+ * computed in fp32 from the bf16 keys; the rest of it is scratch.
  * Errors: those of lvsa_attention; LVSA_ERR_ARG (NULL, misaligned or
  * overlapping workspace), LVSA_ERR_CAPACITY (too small). */
 int lvsa_attention_ws(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,

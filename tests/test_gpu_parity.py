@@ -108,6 +108,20 @@ def test_mid_size_full_output(gpu, case):
     assert_close(o, oa.block_attention(q, k, v, rows), f"mid {case} window-only")
 
 
+def check_key_norms(ws, k, T):
+    """The workspace's key-norm table (largest |k_j| of every (b, h, frame),
+    fp32) against the same maximum taken on the CPU in float64.  A sum of 128
+    positive squares in fp32 through at most 12 dependent roundings, then a
+    square root, stays within 13 units of 2^-24 relative: 2e-6 bounds it."""
+    B, H, N, d = k.shape
+    got = ws[:B * H * T * 4].view(torch.float32).cpu().double().view(B, H, T)
+    norms = k.double().pow(2).sum(-1).sqrt().view(B, H, T, N // T)
+    want = norms.amax(dim=-1)
+    err = ((got - want).abs() / want).max().item()
+    print(f"  key-norm table: max rel err {err:.2e}", flush=True)
+    assert err <= 2e-6, err
+
+
 def test_strided_inputs_and_explicit_scale(gpu):
     # [B, N, H, d] storage viewed as [B, H, N, d] (a model's projection layout).
     B, H, T, P, d, C, W = 1, 4, 10, 96, 128, 4, 2
@@ -120,6 +134,13 @@ def test_strided_inputs_and_explicit_scale(gpu):
     o, rows = run_lib(qd, kd, vd, T, C, W, 3, scale=0.05, out=out)
     ref = oa.block_attention(q.contiguous(), k.contiguous(), v.contiguous(), rows, scale=0.05)
     assert_close(o, ref, "strided scale=0.05")
+    # the workspace path reads K through the same strides for its key norms
+    ws = workspace_for(qd, T)
+    out.fill_(float("nan"))
+    L.lvsa_attention(qd, kd, vd, L.lvsa_build_mask(T, C, W, 3).to(gpu), out=out, scale=0.05, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "strided scale=0.05, workspace")
+    check_key_norms(ws, k, T)
 
 
 def test_shared_kv_heads_by_zero_stride(gpu):
@@ -135,6 +156,11 @@ def test_shared_kv_heads_by_zero_stride(gpu):
     o, rows = run_lib(q.to(gpu), kd, vd, T, C, W, 5)
     ref = oa.block_attention(q, k1.expand(B, H, T * P, d).contiguous(), v1.expand(B, H, T * P, d).contiguous(), rows)
     assert_close(o, ref, "shared K/V head (stride 0)")
+    ws = workspace_for(kd, T)
+    o = L.lvsa_attention(q.to(gpu), kd, vd, L.lvsa_build_mask(T, C, W, 5).to(gpu), workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(o, ref, "shared K/V head (stride 0), workspace")
+    check_key_norms(ws, k1.expand(B, H, T * P, d), T)
 
 
 def test_custom_csr_masks(gpu):
