@@ -437,8 +437,8 @@ void lvsa_attn_fwd(Args a) {
     // broadcast through the first words of LDS tile buffer 1: the first tile
     // loads (buffer 0) do not touch them, and every wave reads them before
     // the barrier that precedes the loads into buffer 1.  (A separate
-    // __shared__ word would take the workgroup past 32 KiB of LDS, which
-    // measured 2.5-6% slower.)
+    // __shared__ word measured 2.5-6% slower, from the code it changes: more
+    // LDS alone, up to 48 KB per workgroup, costs nothing.)
     int *const s_item = reinterpret_cast<int *>(lds + 2 * C::TILE_BYTES);
     if (tid == 0) {
       unsigned xcc;
