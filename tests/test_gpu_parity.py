@@ -381,29 +381,6 @@ def test_workspace_takes_a_fixed_reference_and_falls_back_on_large_norms(gpu):
     assert_close(a[0, 0, toks], oa.block_attention_rows(q, k, v_big, rows, 0, 0, toks), "large values")
 
 
-@pytest.mark.parametrize("name,steps", [("wan13b_6x", (0, 11)), ("wan14b_6x", (0,)), ("wan13b_720p_6x", (0,))],
-                         ids=["wan13b_6x", "wan14b_6x", "wan13b_720p_6x"])
-def test_workspace_full_size_sampled(gpu, name, steps):
-    w = WORKLOADS[name]
-    say("workspace full", w)
-    q, k, v = make_qkv(w, device=gpu)
-    ws = workspace_for(q, w.T)
-    rnd = random.Random(w.seed + 17)
-    heads = [0, w.H - 1]
-    host = {h: (q[:, h:h + 1].cpu(), k[:, h:h + 1].cpu(), v[:, h:h + 1].cpu()) for h in heads}
-    out = torch.empty_like(q)
-    for s in steps:
-        m = L.lvsa_build_mask(w.T, w.C, w.W, s).to(gpu)
-        L.lvsa_attention(q, k, v, m, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        rows = om.key_frames(w.T, w.C, w.W, s)
-        toks = sample_tokens(w.T, w.P, rnd)
-        got = torch.stack([out[0, h, toks].cpu() for h in heads])
-        ref = torch.stack([oa.block_attention_rows(*host[h], rows, 0, 0, toks) for h in heads])
-        assert_close(got, ref, f"ws {name} step {s}")
-        assert torch.isfinite(out).all()
-
-
 @pytest.mark.parametrize("tail_rows", [([5], []), ([3, 1, 3, 4], [2, 2, 0, 7, 6])], ids=["single-and-empty", "malformed"])
 def test_workspace_split_items_merge_their_halves(gpu, tail_rows):
     # With a workspace, the last items of each XCD range run as two halves of
@@ -470,10 +447,10 @@ def test_workspace_results_are_reproducible_and_cover_every_row(gpu):
 FULL = [
     ("wan13b_1x", (0,), (L.LVSA_ROT_MOD_TPER,)),
     ("wan13b_6x", (0, 1, 10, 11, 49), (L.LVSA_ROT_MOD_TPER,)),
-    ("wan14b_6x", (0, 11), (L.LVSA_ROT_MOD_TPER,)),
+    ("wan14b_6x", (0, 5, 10), (L.LVSA_ROT_MOD_TPER,)),
     ("syn_1p5x", (0, 1, 2, 3, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T)),
     ("syn_2x", (0, 1, 3, 4, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_ROT_MOD_T)),
-    ("wan22_720p_6x_h5", (0, 10, 11), (L.LVSA_ROT_MOD_TPER,)),
+    ("wan22_720p_6x_h5", (0, 5, 10, 11), (L.LVSA_ROT_MOD_TPER,)),
     ("wan13b_720p_6x", (0, 49), (L.LVSA_ROT_MOD_TPER, L.LVSA_FIXED_GRID)),
 ]
 
@@ -541,3 +518,199 @@ def test_dense_mask_at_full_size_sampled(gpu):
         ref = oa.block_attention_rows(qh, kh, vh, rows, 0, 0, toks)
         assert_close(a[0, h, toks].cpu(), ref, f"dense, running max, frame {t}")
         assert_close(b[0, h, toks].cpu(), ref, f"dense, workspace, frame {t}")
+
+
+# ---------------- the workspace path at full size: every workload, split items --
+
+BM = 128     # query rows per work item (4 waves x 32 rows)
+N_XCD = 8    # XCDs of the part, one contiguous item range each
+SPLIT_PER_XCD = 96
+
+
+def split_layout(B, H, T, P):
+    """Work items of lvsa_attention_ws, as include/lvsa.h states them: items
+    (b, h, frame, query tile) in that order (query tile fastest) are cut into
+    8 contiguous ranges, and the last min(96, items/32, range/4) items of each
+    range run as two halves merged afterwards.  Returns, per range, the
+    (b, h, t, query tile) of its first split item, its last item and the last
+    item it runs whole (None where a range has no such item)."""
+    q_tiles = (P + BM - 1) // BM
+    n = B * H * T * q_tiles
+    cap = min(SPLIT_PER_XCD, n // (4 * N_XCD))
+    per, rem = divmod(n, N_XCD)
+
+    def decode(item):
+        qt, rest = item % q_tiles, item // q_tiles
+        t, bh = rest % T, rest // T
+        return bh // H, bh % H, t, qt
+
+    out = []
+    for x in range(N_XCD):
+        base = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
+        cnt = per + (1 if x < rem else 0)
+        s = min(cap, cnt // 4)
+        first_split = decode(base + cnt - s) if s else None
+        last = decode(base + cnt - 1) if cnt else None
+        last_whole = decode(base + cnt - s - 1) if cnt - s > 0 else None
+        out.append((first_split, last, last_whole))
+    return out
+
+
+def item_rows(t, qt, P):
+    """The first and last row of each wave of a query tile (frame-relative
+    rows -> tokens)."""
+    rows = set()
+    for w in range(BM // 32):
+        for r in (w * 32, w * 32 + 31):
+            p = qt * BM + r
+            if p < P:
+                rows.add(t * P + p)
+    return rows
+
+
+class HostHeads:
+    """CPU copies of single (b, h) heads of device tensors, made on demand
+    (the oracle works on host tensors)."""
+
+    def __init__(self, q, k, v):
+        self.q, self.k, self.v = q, k, v
+        self.cache = {}
+
+    def __call__(self, b, h):
+        if (b, h) not in self.cache:
+            self.cache[(b, h)] = tuple(x[b:b + 1, h:h + 1].cpu() for x in (self.q, self.k, self.v))
+        return self.cache[(b, h)]
+
+
+def check_sampled(out, heads, rows, samples, what):
+    """samples: {(b, h): sorted tokens}; compares out against the oracle."""
+    got, ref = [], []
+    for (b, h), toks in sorted(samples.items()):
+        toks = sorted(toks)
+        qh, kh, vh = heads(b, h)
+        ref.append(oa.block_attention_rows(qh, kh, vh, rows, 0, 0, toks))
+        got.append(out[b, h, toks].cpu())
+    assert_close(torch.cat(got), torch.cat(ref), what)
+
+
+@pytest.mark.parametrize("name,steps,flag_list", FULL, ids=[f[0] for f in FULL])
+def test_workspace_full_size_sampled(gpu, name, steps, flag_list):
+    # The benchmarked path at every workload shape, step list and rotation
+    # flag of the running-max test above.  Sampled rows: the structured and
+    # random rows of heads 0 and H-1, plus, in each of the 8 XCD ranges, the
+    # wave-edge rows of the first and last item run as two halves and of the
+    # last item run whole (so every range's merged items are checked).
+    w = WORKLOADS[name]
+    say("workspace full", w)
+    q, k, v = make_qkv(w, device=gpu)
+    ws = workspace_for(q, w.T)
+    heads = HostHeads(q, k, v)
+    rnd = random.Random(w.seed + 17)
+    layout = split_layout(w.B, w.H, w.T, w.P)
+    n_split = sum(1 for f, _, _ in layout if f is not None)
+    print(f"  XCD ranges with split items: {n_split} of {N_XCD}", flush=True)
+    out = torch.empty_like(q)
+    for flags in flag_list:
+        for s in steps:
+            m = L.lvsa_build_mask(w.T, w.C, w.W, s, flags)
+            rp, ci, _ = om.build_mask(w.T, w.C, w.W, s, flags)
+            assert m.row_ptr.tolist() == rp and m.col_idx.tolist() == ci
+            out.fill_(float("nan"))
+            L.lvsa_attention(q, k, v, m.to(gpu), out=out, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.isfinite(out).all()  # every row written, none overflowed
+            rows = om.key_frames(w.T, w.C, w.W, s, flags)
+            samples = {}
+            toks = sample_tokens(w.T, w.P, rnd)
+            for h in (0, w.H - 1):
+                samples.setdefault((0, h), set()).update(toks)
+            for item in (it for rng in layout for it in rng if it is not None):
+                b, h, t, qt = item
+                samples.setdefault((b, h), set()).update(item_rows(t, qt, w.P))
+            check_sampled(out, heads, rows, samples, f"ws {name} step {s} flags {flags}")
+
+
+@pytest.mark.parametrize("T,P,d,C,W,H", [(8, 64, 64, 4, 2, 2), (121, 1560, 128, 21, 9, 8)],
+                         ids=["tiny-shape", "wan-6x-shape-8heads"])
+def test_workspace_probe_zero_keys_reads_whole_mask(gpu, T, P, d, C, W, H):
+    # The K = 0 read-back probe of the whole output through lvsa_attention_ws.
+    # With 8 heads at the 121-frame shape every XCD range has items run as
+    # two halves, so the merged halves of every range are read back too.
+    # Every weight is 1, so out[i, f] = 1/|A(t)| exactly (bf16) for f in A(t)
+    # and 0 otherwise.  Also V = 1 (out = 1 within one bf16 step below 1).
+    say("workspace probe K=0, V=1", (T, P, d, C, W, H))
+    N = T * P
+    layout = split_layout(1, H, T, P)
+    assert all(f is not None for f, _, _ in layout) or T < 100
+    q = make_random((1, H, N, d), 511).to(gpu)
+    k = torch.zeros(1, H, N, d, dtype=torch.bfloat16, device=gpu)
+    frame = torch.arange(N, device=gpu) // P
+    v = torch.zeros(1, H, N, d, dtype=torch.bfloat16, device=gpu)
+    v[:, :, torch.arange(N, device=gpu), frame] = 1.0
+    ws = workspace_for(q, T)
+    out = torch.empty_like(q)
+    for s in (0, 1, 5):
+        rows = om.key_frames(T, C, W, s)
+        out.fill_(float("nan"))
+        L.lvsa_attention(q, k, v, L.lvsa_build_mask(T, C, W, s).to(gpu), out=out, workspace=ws)
+        torch.cuda.synchronize()
+        expect = torch.zeros(T, d)
+        for t, r in enumerate(rows):
+            expect[t, r] = float(torch.tensor(1.0 / len(r)).to(torch.bfloat16))
+        expect = expect.to(gpu)
+        err = (out.float().view(H, T, P, d) - expect.view(1, T, 1, d)).abs().amax().item()
+        print(f"  step {s}: max err {err:.3e} over the whole output", flush=True)
+        assert err <= 2e-4
+    ones = torch.ones_like(v)
+    out.fill_(float("nan"))
+    L.lvsa_attention(q, k, ones, L.lvsa_build_mask(T, C, W, 3).to(gpu), out=out, workspace=ws)
+    torch.cuda.synchronize()
+    err = (out.float() - 1.0).abs().amax().item()
+    print(f"  V = 1: max |out - 1| {err:.3e} over the whole output", flush=True)
+    assert err <= 2.0 ** -8
+
+
+# ---------------------------------------------------------- NaN inputs --
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["running-max", "workspace"])
+def test_nan_stays_in_the_rows_that_read_it(gpu, use_ws):
+    # A NaN in one query row, in one key of one frame, and in one value of
+    # one frame (each in a different head).  Only that query's output row, and
+    # the rows of query frames whose A(t) contains the poisoned key/value
+    # frame, may be non-finite; every other row must be finite and within the
+    # bars.  8 heads x 8 frames x 2 query tiles: on the workspace path the
+    # last 4 items of each XCD range run as merged halves, so the poisoned
+    # rows reach the merge too.
+    B, H, T, P, d, C, W, step = 1, 8, 8, 150, 128, 4, 2, 3
+    say("NaN rows", (B, H, T, P, d, C, W), "step", step, "workspace" if use_ws else "running max")
+    q = make_random((B, H, T * P, d), 701)
+    k = make_random((B, H, T * P, d), 702)
+    v = make_random((B, H, T * P, d), 703)
+    rows = om.key_frames(T, C, W, step)
+    hq, iq = 1, 3 * P + 77            # query row 77 of frame 3, head 1
+    hk, fk = 4, 5                     # key 10 of frame 5, head 4
+    hv, fv = 7, 6                     # value 149 of frame 6, head 7 (the frame's last token)
+    q[0, hq, iq, 9] = float("nan")
+    k[0, hk, fk * P + 10, 100] = float("nan")
+    v[0, hv, fv * P + 149, 3] = float("nan")
+    qd, kd, vd = q.to(gpu), k.to(gpu), v.to(gpu)
+    m = L.lvsa_build_mask(T, C, W, step).to(gpu)
+    ws = workspace_for(qd, T) if use_ws else None
+    o = torch.full_like(qd, float("nan"))
+    L.lvsa_attention(qd, kd, vd, m, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    allowed = torch.zeros(B, H, T * P, dtype=torch.bool)
+    allowed[0, hq, iq] = True
+    for h, f in ((hk, fk), (hv, fv)):
+        for t, r in enumerate(rows):
+            if f in r:
+                allowed[0, h, t * P:(t + 1) * P] = True
+    finite = torch.isfinite(o.float()).all(dim=-1)
+    assert bool(finite[~allowed].all()), "non-finite output outside the rows that read a NaN"
+    ref = oa.block_attention(q, k, v, rows)
+    keep = ~allowed
+    assert_close(o[keep], ref[keep], "rows that read no NaN")
+    print(f"  rows allowed non-finite: {int(allowed.sum())}, of them non-finite: "
+          f"{int((~finite & allowed).sum())}", flush=True)
