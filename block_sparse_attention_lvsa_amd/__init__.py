@@ -19,6 +19,8 @@ Functions with the ABI's names:
   lvsa_attention(q, k, v, mask_dev, out=None, scale=None, stream=None, workspace=None) -> out
       (with a workspace: the C ABI's lvsa_attention_ws)
   lvsa_attention_workspace_bytes(B, H, N, D, T) -> int
+  lvsa_attention_ws_static(q, k, v, mask_dev, out, scale=None, stream=None) -> out
+      (the workspace path on the library's static device scratch; allocates nothing)
 
 ``Mask.to(device)`` copies the CSR arrays (``non_blocking`` on the current
 stream) for ``lvsa_attention``.  ``MaskSteps`` holds the masks of a run of
@@ -46,6 +48,7 @@ LVSA_FIXED_GRID = 2
 LVSA_WINDOW_ONLY = 3
 
 LVSA_DTYPE_BF16 = 1
+LVSA_STATIC_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblvsa.so")
 
@@ -110,6 +113,10 @@ def library() -> ctypes.CDLL:
         lib.lvsa_attention_ws.argtypes = [ctypes.POINTER(LvsaTensor)] * 3 + [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.POINTER(LvsaTensor), ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.lvsa_attention_ws_static.restype = ctypes.c_int
+        lib.lvsa_attention_ws_static.argtypes = [ctypes.POINTER(LvsaTensor)] * 3 + [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.POINTER(LvsaTensor), ctypes.c_float, ctypes.c_void_p]
         lib.lvsa_attention_workspace_bytes.restype = ctypes.c_int
         lib.lvsa_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                        ctypes.c_int64, ctypes.c_int32,
@@ -287,4 +294,33 @@ def lvsa_attention(q, k, v, mask: Mask, out=None, scale: Optional[float] = None,
             nbytes = workspace.numel() * workspace.element_size()
             _check(library().lvsa_attention_ws(*args, ctypes.c_void_p(workspace.data_ptr()), nbytes,
                                                ctypes.c_void_p(sp)))
+    return out
+
+
+def lvsa_attention_ws_static(q, k, v, mask: Mask, out, scale: Optional[float] = None, stream=None):
+    """lvsa_attention with the library's static device scratch as its
+    workspace (the C ABI's lvsa_attention_ws_static): nothing is allocated,
+    here or in the library, so ``out`` must be given.  Calls that can overlap
+    on one GPU race on the shared scratch (see include/lvsa.h)."""
+    import torch
+    if out is None:
+        raise LvsaValueError(LVSA_ERR_ARG, "out: required (this entry point allocates nothing)")
+    if mask.row_ptr.numel() != mask.T + 1:
+        raise LvsaValueError(LVSA_ERR_ARG, f"mask.row_ptr has {mask.row_ptr.numel()} entries, need T+1")
+    for name, t in (("row_ptr", mask.row_ptr), ("col_idx", mask.col_idx)):
+        if t.device != q.device or t.dtype != torch.int32 or not t.is_contiguous():
+            raise LvsaValueError(LVSA_ERR_ARG, f"mask.{name}: need contiguous int32 on {q.device}")
+    rq, rk, rv, ro = (_tensor_record(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.device != q.device:
+            raise LvsaValueError(LVSA_ERR_ARG, f"{name}: on {t.device}, q on {q.device}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        _check(library().lvsa_attention_ws_static(
+            ctypes.byref(rq), ctypes.byref(rk), ctypes.byref(rv),
+            ctypes.c_void_p(mask.row_ptr.data_ptr()), ctypes.c_void_p(mask.col_idx.data_ptr()),
+            mask.T, mask.col_idx.numel(), ctypes.byref(ro), 0.0 if scale is None else float(scale),
+            ctypes.c_void_p(sp)))
     return out

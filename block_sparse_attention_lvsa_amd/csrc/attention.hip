@@ -62,6 +62,16 @@
 
 #include "lvsa_internal.h"
 
+// Device scratch of lvsa_attention_ws_static, for callers that cannot
+// allocate: the key-norm table, the work counters and the partial records of
+// lvsa_attention_ws, at most kStaticScratchBytes.  Every GPU the library runs
+// on holds its own copy until the process ends.  Host code never uses this
+// name as a device address: it takes the address per device from
+// hipGetSymbolAddress (static_scratch_ptr below).
+static constexpr int64_t kStaticScratchBytes = LVSA_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -799,6 +809,29 @@ int check_device(int *dev_out) {
   return LVSA_OK;
 }
 
+// Device address of `scratch` on each device, taken once per device with
+// that device current.
+struct ScratchAddr {
+  std::once_flag once[64];
+  void *ptr[64] = {};
+  hipError_t err[64] = {};
+};
+ScratchAddr g_scratch;
+
+int static_scratch_ptr(int dev, void **out) {
+  std::call_once(g_scratch.once[dev], [dev]() {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch.err[dev] = e;
+    g_scratch.ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch.err[dev] != hipSuccess || !g_scratch.ptr[dev])
+    return lvsa::fail(LVSA_ERR_HIP, "device %d: no address for the static scratch (%s)", dev,
+                      hipGetErrorString(g_scratch.err[dev]));
+  *out = g_scratch.ptr[dev];
+  return LVSA_OK;
+}
+
 int check_tensor(const lvsa_tensor *x, const char *name) {
   if (!x || !x->data) return lvsa::fail(LVSA_ERR_ARG, "%s: NULL tensor or data pointer", name);
   if (x->dtype != LVSA_DTYPE_BF16) return lvsa::fail(LVSA_ERR_DTYPE, "%s: dtype %d, only bf16 is supported", name, x->dtype);
@@ -892,16 +925,19 @@ int64_t items_for(int64_t B, int64_t H, int64_t N, int64_t T) {
 }
 // At most a quarter of every XCD range is split.
 int32_t split_cap_for(int64_t items) { return (int32_t)std::min<int64_t>(kSplitPerXcd, items / (4 * kNumXcd)); }
+// Bytes of partial records per unit of split_cap (one slot per XCD).
+int64_t split_unit_bytes(int64_t D) { return (int64_t)kNumXcd * 2 * LVSA_NW * 64 * kPartialFloats((int)D) * 4; }
+int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T, int32_t split_cap) {
+  return norms_bytes_for(B, H, T) + 256 + split_cap * split_unit_bytes(D);
+}
 int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T) {
-  const int64_t partial =
-      (int64_t)kNumXcd * split_cap_for(items_for(B, H, N, T)) * 2 * LVSA_NW * 64 * kPartialFloats((int)D) * 4;
-  return norms_bytes_for(B, H, T) + 256 + partial;
+  return workspace_bytes_for(B, H, N, D, T, split_cap_for(items_for(B, H, N, T)));
 }
 
 int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
                    const int32_t *row_ptr_dev, const int32_t *col_idx_dev, int32_t T, int32_t nnz,
                    lvsa_tensor *out, float scale, void *workspace, int64_t workspace_bytes, bool use_ws,
-                   void *stream) {
+                   void *stream, int32_t split_cap_limit = -1) {
   int rc;
   if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k")) || (rc = check_tensor(v, "v")) ||
       (rc = check_tensor(out, "out")))
@@ -923,8 +959,11 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
     std::memcpy(&bits, &scale, sizeof bits);
     if ((bits & 0x7f800000u) == 0x7f800000u) return lvsa::fail(LVSA_ERR_ARG, "scale is not finite");
   }
+  int32_t split_cap = 0;
   if (use_ws) {
-    const int64_t need = workspace_bytes_for(q->B, q->H, q->N, q->D, T);
+    split_cap = split_cap_for(items_for(q->B, q->H, q->N, T));
+    if (split_cap_limit >= 0) split_cap = std::min(split_cap, split_cap_limit);
+    const int64_t need = workspace_bytes_for(q->B, q->H, q->N, q->D, T, split_cap);
     if (!workspace) return lvsa::fail(LVSA_ERR_ARG, "workspace is NULL");
     // the partial records are written and read 16 bytes at a time
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return lvsa::fail(LVSA_ERR_ARG, "workspace not 16-byte aligned");
@@ -973,7 +1012,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                      : nullptr;
   a.partial = use_ws ? reinterpret_cast<float *>(static_cast<char *>(workspace) + norms_bytes_for(q->B, q->H, T) + 256)
                      : nullptr;
-  a.split_cap = use_ws ? split_cap_for(n_wg) : 0;
+  a.split_cap = split_cap;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128) return launch<128, NW>(a, s);
@@ -1007,4 +1046,29 @@ extern "C" int lvsa_attention_ws(const lvsa_tensor *q, const lvsa_tensor *k, con
                                  void *workspace, int64_t workspace_bytes, void *stream) {
   return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, workspace, workspace_bytes, true,
                         stream);
+}
+
+extern "C" int lvsa_attention_ws_static(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                                        const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                                        int32_t T, int32_t nnz, lvsa_tensor *out, float scale, void *stream) {
+  int rc, dev;
+  if ((rc = check_tensor(q, "q"))) return rc;
+  if (T < 1) return lvsa::fail(LVSA_ERR_ARG, "T=%d: need T >= 1", T);
+  if (q->N % T) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld is not a multiple of T=%d", (long long)q->N, T);
+  // The key-norm table (one float per (b, h, frame)) and the counters must
+  // fit; the split items take what is left (fewer items than
+  // lvsa_attention_ws splits, when the room is smaller).
+  const double frames = (double)q->B * (double)q->H * (double)T;
+  if (frames * 4.0 + 512.0 > (double)kStaticScratchBytes)
+    return lvsa::fail(LVSA_ERR_CAPACITY,
+                      "B*H*T = %.0f (b, h, frame) entries do not fit the static scratch of %lld bytes (at most "
+                      "%lld); use lvsa_attention_ws with a caller workspace",
+                      frames, (long long)kStaticScratchBytes, (long long)((kStaticScratchBytes - 512) / 4));
+  if ((rc = check_device(&dev))) return rc;
+  void *ws;
+  if ((rc = static_scratch_ptr(dev, &ws))) return rc;
+  const int64_t fixed = norms_bytes_for(q->B, q->H, T) + 256;
+  const int32_t cap = (int32_t)std::min<int64_t>(INT32_MAX, (kStaticScratchBytes - fixed) / split_unit_bytes(q->D));
+  return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, ws, kStaticScratchBytes, true,
+                        stream, cap);
 }

@@ -245,6 +245,29 @@ int lvsa_attention_ws(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_ten
                       int32_t T, int32_t nnz, lvsa_tensor *out, float scale,
                       void *workspace, int64_t workspace_bytes, void *stream);
 
+/* lvsa_attention_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid it).  It calls no allocating
+ * routine: the workspace is the library's own static device array of
+ * LVSA_STATIC_SCRATCH_BYTES bytes, one per GPU, held until the process ends.
+ *
+ * Same computation, arguments and errors as lvsa_attention_ws minus the
+ * workspace arguments.  The key-norm table (one float per (b, h, frame)) and
+ * the work counters must fit the array: B·H·T <= (LVSA_STATIC_SCRATCH_BYTES
+ * - 512) / 4, else LVSA_ERR_CAPACITY and nothing is launched.  The items run
+ * as two merged halves are limited to what the rest of the array holds, so
+ * results can differ from lvsa_attention_ws in rounding (same accuracy).
+ * The counters are cleared by the call's own first kernel.
+ *
+ * Every call on one GPU uses that GPU's single array: calls whose kernels
+ * can overlap on one GPU (different streams, or several host threads without
+ * ordering) race and give wrong results.  Calls ordered on one stream are
+ * safe.  The array keeps the last call's contents. */
+#define LVSA_STATIC_SCRATCH_BYTES (16 << 20)
+int lvsa_attention_ws_static(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
+                             const int32_t *row_ptr_dev, const int32_t *col_idx_dev,
+                             int32_t T, int32_t nnz, lvsa_tensor *out, float scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

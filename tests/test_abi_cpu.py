@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"lvsa_version", "lvsa_last_error", "lvsa_mask_nnz", "lvsa_build_mask",
                           "lvsa_build_mask_steps", "lvsa_validate_mask", "lvsa_attention",
-                          "lvsa_attention_ws", "lvsa_attention_workspace_bytes"}
+                          "lvsa_attention_ws", "lvsa_attention_workspace_bytes", "lvsa_attention_ws_static"}
     for n in names:
         assert hasattr(lib, n), n
     assert L.lvsa_version() == 2
@@ -226,6 +226,37 @@ def test_workspace_errors_are_reported_before_any_device_work():
     assert _attn_ws(q, k, v, o, base + 16, need) == L.LVSA_ERR_ARG        # inside q
     assert "overlaps" in L.lvsa_last_error()
     assert _attn_ws(_rec(base, dtype=0), k, v, o, ws, need) == L.LVSA_ERR_DTYPE  # the plain checks still apply
+
+
+def _attn_static(q, k, v, o, T=8, nnz=32, rp=0x1000, ci=0x2000):
+    lib = L.library()
+    return lib.lvsa_attention_ws_static(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                        ctypes.c_void_p(rp), ctypes.c_void_p(ci), T, nnz,
+                                        ctypes.byref(o), 0.0, None)
+
+
+def test_static_scratch_entry_point_errors_before_any_device_work():
+    # lvsa_attention_ws_static: the argument checks of lvsa_attention_ws, and
+    # a key-norm table larger than the static scratch refused on the host.
+    base = 1 << 32
+    sz = 2 * 512 * 64 * 2
+    q, k, v, o = (_rec(base + i * sz) for i in range(4))
+    assert _attn_static(q, k, v, o, T=0) == L.LVSA_ERR_ARG
+    assert _attn_static(q, k, v, o, T=7) == L.LVSA_ERR_SHAPE
+    assert _attn_static(_rec(base, dtype=0), k, v, o) == L.LVSA_ERR_DTYPE
+    # 4,200 heads x 1,024 frames (stride-0 views): 17.2 MB of norms > 16 MiB
+    big = [_rec(base + i * sz, H=4200, N=1024, sh=0) for i in range(4)]
+    assert _attn_static(*big, T=1024, nnz=4096) == L.LVSA_ERR_CAPACITY
+    assert "static scratch" in L.lvsa_last_error()
+    assert L.LVSA_STATIC_SCRATCH_BYTES == 16 << 20
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_static_scratch_entry_point_without_device_reports_hip_error():
+    base = 1 << 32
+    sz = 2 * 512 * 64 * 2
+    q, k, v, o = (_rec(base + i * sz) for i in range(4))
+    assert _attn_static(q, k, v, o) == L.LVSA_ERR_HIP
 
 
 def test_attention_rejects_self_overlapping_output():
