@@ -53,6 +53,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -81,12 +82,9 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-// Tuning knobs (compile-time): waves per workgroup, the register budget
-// expressed as resident waves per SIMD, keys per tile, and how many K operand
-// reads run ahead of the Q·Kᵀ MFMA chain.
-#ifndef LVSA_NW
-#define LVSA_NW 4
-#endif
+// Tuning knobs (compile-time): the register budget expressed as resident
+// waves per SIMD, keys per tile, and how many K operand reads run ahead of
+// the Q·Kᵀ MFMA chain.
 #ifndef LVSA_WAVES_PER_SIMD
 #define LVSA_WAVES_PER_SIMD 3
 #endif
@@ -133,28 +131,75 @@ struct Args {
 typedef const __attribute__((address_space(4))) int32_t *const_i32p;
 typedef const __attribute__((address_space(4))) float *const_f32p;
 
-// Walks one CSR row and yields maximal runs of consecutive frames as token
-// ranges [ks, ke).  Every value is wave-uniform (scalar registers).  An entry
-// outside [0, T), or not above the last frame taken, is skipped, so a
-// malformed row never causes an out-of-range read and never repeats a frame.
-struct RunIter {
+// One CSR row's entries, in order.  An entry outside [0, T), or not above
+// the last entry taken, is skipped, so a malformed row never causes an
+// out-of-range read and never repeats a frame.  Every value is wave-uniform
+// (scalar registers).
+struct RowCursor {
   const_i32p cols;
-  int32_t e, e_end, T, P;
+  int32_t e, e_end, T;
   int32_t last;  // last frame taken (-1 before the first)
-  int32_t ks, ke;
 
-  __device__ bool next_run() {
+  // The next frame the row keeps, or T when it has none left.
+  __device__ int32_t peek() {
     while (e < e_end) {
-      const int32_t f = cols[e++];
-      if (f <= last || f >= T) continue;
-      int32_t f1 = f;
-      while (e < e_end && f1 + 1 < T && cols[e] == f1 + 1) { ++f1; ++e; }
-      last = f1;
-      ks = f * P;
-      ke = (f1 + 1) * P;
-      return true;
+      const int32_t f = cols[e];
+      if (f > last && f < T) return f;
+      ++e;
     }
-    return false;
+    return T;
+  }
+  __device__ void take(int32_t f) {
+    last = f;
+    ++e;
+  }
+};
+
+// The key walk of a workgroup whose query rows lie in frames t0 and t1
+// (t1 = t0, or t0 + 1 when the rows cross a frame boundary): the union of
+// the two CSR rows, in ascending frame order, as segments of consecutive
+// frames with the same membership (bit 0: the frame is in A(t0), bit 1: in
+// A(t1); with one row both bits are set).  Tokens are frame-major, so a
+// segment of frames [f0, f1] is the one contiguous token range
+// [f0·P, (f1+1)·P).  Frames at or above f_hi are not walked.
+struct SegIter {
+  RowCursor r0, r1;
+  int32_t f_hi, P;
+  bool two;
+  int32_t ks, ke, mem;
+
+  __device__ int32_t peek1() { return two ? r1.peek() : r0.T; }
+  __device__ int members(int32_t f, int32_t a0, int32_t a1) const {
+    return two ? ((a0 == f ? 1 : 0) | (a1 == f ? 2 : 0)) : (a0 == f ? 3 : 0);
+  }
+  __device__ void take(int32_t f, int32_t a0, int32_t a1) {
+    if (a0 == f) r0.take(f);
+    if (two && a1 == f) r1.take(f);
+  }
+  // Skips every frame below f_lo (the second half of a split walk).
+  __device__ void skip_below(int32_t f_lo) {
+    while (r0.peek() < f_lo) r0.take(r0.peek());
+    if (two)
+      while (r1.peek() < f_lo) r1.take(r1.peek());
+  }
+  __device__ bool next() {
+    int32_t a0 = r0.peek(), a1 = peek1();
+    const int32_t fs = min(a0, a1);
+    if (fs >= f_hi) return false;
+    const int m = members(fs, a0, a1);
+    take(fs, a0, a1);
+    int32_t fe = fs;
+    while (fe + 1 < f_hi) {
+      a0 = r0.peek();
+      a1 = peek1();
+      if (members(fe + 1, a0, a1) != m) break;
+      take(fe + 1, a0, a1);
+      ++fe;
+    }
+    ks = fs * P;
+    ke = (fe + 1) * P;
+    mem = m;
+    return true;
   }
 };
 
@@ -191,12 +236,13 @@ struct Cfg {
   static constexpr int ROWB = D * 2;          // bytes per key row
   static constexpr int TILE_BYTES = BN * ROWB;
   static constexpr int LOADS = TILE_BYTES / 1024;      // 1 KB wave loads per tile
-  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  static constexpr int LOADS_PER_WAVE = LOADS >= NW ? LOADS / NW : 1;
+  static constexpr int NLOADERS = LOADS / LOADS_PER_WAVE;  // waves that issue the tile loads
   static constexpr int VSW = CH / 4;          // V swizzle step
   static constexpr int KEYS_PER_LOAD = 64 / CH;       // keys per 1 KB wave load
   static constexpr int STAGES = 2;                    // LDS tile buffers (loads run one tile ahead)
   static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES; // {K, V} × STAGES
-  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+  static_assert(LOADS % NW == 0 || NW > LOADS, "tile loads must split evenly over the loading waves");
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -282,6 +328,7 @@ struct Block {
     const u16 *tb = base + (int64_t)pos * sn;
     const int nrec = ((kv - 1) * sn + D) * 2;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, nrec, kBufferFlags);
+    if (wave >= C::NLOADERS) return;  // wave-uniform
     char *dst = lds + (IS_V ? kTileOffV(buf) : kTileOffK(buf)) + wave * C::LOADS_PER_WAVE * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
@@ -403,20 +450,80 @@ struct Block {
       }
   }
 
-  // One key tile from LDS buffer BUF.
+  // Removes the whole tile from the rows of the lanes not set in `keep`
+  // (a wave whose rows cross a frame boundary, on key frames only one of
+  // the two frames attends).
+  __device__ __forceinline__ void mask_lanes(f32x16_t (&sc)[C::KB], uint64_t keep) {
+    asm volatile("" ::: "memory");  // keep the wave-uniform branch around it a branch
+    const bool ok = (keep >> lane) & 1;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
+  }
+
+  // One key tile from LDS buffer BUF.  lane_mask: whether only the lanes in
+  // `keep` attend it.
   template <int BUF, bool FIXED>
-  __device__ __forceinline__ void tile(int kv) {
+  __device__ __forceinline__ void tile(int kv, bool lane_mask, uint64_t keep) {
     f32x16_t sc[C::KB];
     bf16x8_t pb[2 * C::KB];
     qk<BUF, FIXED>(sc);
     mask_tail(sc, kv);
+    if (lane_mask) mask_lanes(sc, keep);
     if constexpr (!FIXED) fold_max(sc);
     probs<FIXED>(sc, pb);
     pv<BUF>(pb);
   }
 };
 
-template <int D, int NW>
+// A work item's query rows.  SPAN = false: query tile qt (BM rows) of frame
+// t of (b, h), items ordered (b, h, t, qt).  SPAN = true (frames of at least
+// BM tokens): rows [qt·BM, qt·BM + BM) of the (b, h) token sequence, items
+// ordered (b, h, qt); such a tile lies in frame t0 and possibly t1 = t0 + 1.
+struct Item {
+  int b, h, bh, t0, t1, tok0, tok_end;
+};
+
+template <int BM, bool SPAN>
+__device__ __forceinline__ Item decode_item(const Args &a, int item) {
+  Item it;
+  const int qt = item % a.q_tiles;
+  const int rest = item / a.q_tiles;
+  if (SPAN) {
+    it.bh = rest;
+    it.tok0 = qt * BM;
+    it.tok_end = min(a.T * a.P, it.tok0 + BM);
+    it.t0 = it.tok0 / a.P;
+    it.t1 = (it.tok_end - 1) / a.P;
+  } else {
+    const int t = rest % a.T;
+    it.bh = rest / a.T;
+    it.tok0 = t * a.P + qt * BM;
+    it.tok_end = (t + 1) * a.P;
+    it.t0 = it.t1 = t;
+  }
+  it.h = it.bh % a.H;
+  it.b = it.bh / a.H;
+  return it;
+}
+
+// CSR row t, its offsets clamped to [0, nnz].
+__device__ __forceinline__ RowCursor row_cursor(const Args &a, int t) {
+  const const_i32p rp = (const_i32p)a.row_ptr;
+  int32_t rb = rp[t], re = rp[t + 1];
+  rb = rb < 0 ? 0 : (rb > a.nnz ? a.nnz : rb);
+  re = re < rb ? rb : (re > a.nnz ? a.nnz : re);
+  RowCursor c;
+  c.cols = (const_i32p)a.col_idx;
+  c.e = rb;
+  c.e_end = re;
+  c.T = a.T;
+  c.last = -1;
+  return c;
+}
+
+template <int D, int NW, bool SPAN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
 void lvsa_attn_fwd(Args a) {
   using C = Cfg<D, NW>;
@@ -488,23 +595,17 @@ void lvsa_attn_fwd(Args a) {
     xcd_range(a.n_wg, x, &base, &cnt);
     item = base + j;
   }
-  const int qt = item % a.q_tiles;
-  const int rest = item / a.q_tiles;
-  const int t = rest % a.T;
-  const int bh = rest / a.T;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  const Item wi = decode_item<C::BM, SPAN>(a, item);
   const int P = a.P;
-
-  const u16 *kbase = a.k + (int64_t)b * a.k_sb + (int64_t)h * a.k_sh;
-  const u16 *vbase = a.v + (int64_t)b * a.v_sb + (int64_t)h * a.v_sh;
+  const u16 *kbase = a.k + (int64_t)wi.b * a.k_sb + (int64_t)wi.h * a.k_sh;
+  const u16 *vbase = a.v + (int64_t)wi.b * a.v_sb + (int64_t)wi.h * a.v_sh;
 
   // ---- Q fragments: the wave's 32 rows × D, B-operand layout
-  const int row0 = qt * C::BM + blk.wave * 32;  // first row of this wave within frame t
+  const int row0 = wi.tok0 + blk.wave * 32;  // token of the wave's first row
+  const int my_row = row0 + blk.l32;
   {
-    const int r = row0 + blk.l32;
-    const bool ok = r < P;
-    const u16 *qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + ((int64_t)t * P + (ok ? r : 0)) * a.q_sn +
+    const bool ok = my_row < wi.tok_end;
+    const u16 *qp = a.q + (int64_t)wi.b * a.q_sb + (int64_t)wi.h * a.q_sh + (int64_t)(ok ? my_row : 0) * a.q_sn +
                     blk.hf * 8;
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc) {
@@ -515,61 +616,61 @@ void lvsa_attn_fwd(Args a) {
   }
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) blk.oacc[i] = f32x16_t{};
-  blk.m_run = -INFINITY;
+  // A finite start: a lane whose first tiles are all masked out (see
+  // mask_lanes) then gets probabilities 2^-inf = 0 rather than NaN.
+  blk.m_run = -FLT_MAX;
   blk.l_run = 0.f;
   blk.init_offsets(a.k_sn, a.v_sn);
-  // Whether the wave has rows inside the frame (the last query tile of a
-  // frame may not fill every wave), as a scalar, so the per-tile test is a
-  // scalar branch rather than a vector compare.
-  const int compute = __builtin_amdgcn_readfirstlane(row0 < P ? 1 : 0);
+  // Whether the wave has rows in the tile (the last tile of a frame or of
+  // the sequence may not fill every wave), as a scalar, so the per-tile test
+  // is a scalar branch rather than a vector compare.
+  const int compute = __builtin_amdgcn_readfirstlane(row0 < wi.tok_end ? 1 : 0);
+  // Which of the walk's frame memberships the wave's rows need (bit 0: rows
+  // in t0, bit 1: rows in t1), and, for a wave whose rows cross the frame
+  // boundary, the lanes whose rows lie in t1.
+  const bool two = wi.t1 != wi.t0;
+  int need = 3;
+  uint64_t lanes_t1 = 0;
+  if (SPAN && two && compute) {
+    const int f_first = row0 / P;
+    const int f_last = min(row0 + 31, wi.tok_end - 1) / P;
+    need = f_first == f_last ? (f_first == wi.t0 ? 1 : 2) : 3;
+    lanes_t1 = __builtin_amdgcn_ballot_w64(my_row / P == wi.t1);
+  }
+  need = __builtin_amdgcn_readfirstlane(need);
 
-  // ---- CSR row -> runs of key frames
-  RunIter it;
-  int32_t rb, re;  // the whole CSR row
-  {
-    const const_i32p rp = (const_i32p)a.row_ptr;
-    rb = rp[t];
-    re = rp[t + 1];
-    rb = rb < 0 ? 0 : (rb > a.nnz ? a.nnz : rb);
-    re = re < rb ? rb : (re > a.nnz ? a.nnz : re);
-    it.cols = (const_i32p)a.col_idx;
-    it.e = rb;
-    it.e_end = re;
-    it.T = a.T;
-    it.P = P;
-    it.last = -1;
-    it.ks = it.ke = 0;
-  }
-  int n_tiles = 0;  // tiles of the whole row
-  {
-    RunIter c = it;
-    while (c.next_run()) n_tiles += (c.ke - c.ks + C::BN - 1) / C::BN;
-  }
-  int n_walk = n_tiles;  // tiles this workgroup walks
+  // ---- the key walk: the union of the rows of t0 and t1, split at frame fm
+  // for the two halves of a split item (the first half walks the frames
+  // below fm, the second the rest, so that together they walk exactly what
+  // the whole walk does)
+  SegIter it;
+  it.r0 = row_cursor(a, wi.t0);
+  it.r1 = two ? row_cursor(a, wi.t1) : it.r0;
+  it.two = two;
+  it.P = P;
+  it.f_hi = a.T;
+  it.ks = it.ke = it.mem = 0;
   if (half >= 0) {
-    // A half walks entries [rb, mid) or [mid, re) of the row, the second
-    // starting from the walk's state at mid, so that together they keep
-    // exactly the entries the whole walk keeps.
-    const int32_t mid = rb + (re - rb) / 2;
-    RunIter c = it;
-    c.e_end = mid;
-    int first = 0;
-    while (c.next_run()) first += (c.ke - c.ks + C::BN - 1) / C::BN;
-    if (half == 0) {
-      it.e_end = mid;
-      n_walk = first;
-    } else {
-      it.e = mid;
-      it.last = c.last;
-      n_walk = 0;
-      RunIter d = it;
-      while (d.next_run()) n_walk += (d.ke - d.ks + C::BN - 1) / C::BN;
-    }
+    // fm: the middle entry of t0's row (any frame partitions the walk; the
+    // middle one halves it for well-formed rows)
+    const int32_t rb0 = it.r0.e, re0 = it.r0.e_end;
+    const int32_t mid = rb0 + (re0 - rb0) / 2;
+    int32_t fm = re0 > rb0 ? it.r0.cols[mid] : 0;
+    fm = fm < 0 ? 0 : (fm > a.T ? a.T : fm);
+    if (half == 0)
+      it.f_hi = fm;
+    else
+      it.skip_below(fm);
+  }
+  int n_walk = 0;  // tiles this workgroup walks
+  {
+    SegIter c = it;
+    while (c.next()) n_walk += (c.ke - c.ks + C::BN - 1) / C::BN;
   }
 
   // ---- softmax reference.  Without a key-norm table: the running max,
   // raised lazily.  With one: by Cauchy-Schwarz every score of query i lies
-  // within ±|q_i|·K, K the largest key norm over the row's frames, so
+  // within ±|q_i|·K, K the largest key norm over the walk's frames, so
   // R_i = scale·log2e·|q_i|·K·(1 + 2^-8) bounds every exponent (the factor
   // covers the rounding of the fp32 norms and of the MFMA dot products).  A
   // wave whose lanes all have 2·R_i <= kMaxRefGap (the bound cannot sit more
@@ -578,11 +679,16 @@ void lvsa_attn_fwd(Args a) {
   // Q·Kᵀ chain's initial accumulator.  Other waves keep the running max.
   bool fixed = false;
   if (a.knorm) {
-    const const_f32p fn = (const_f32p)(a.knorm + (int64_t)bh * a.T);
+    const const_f32p fn = (const_f32p)(a.knorm + (int64_t)wi.bh * a.T);
     float kn = 0.f;
-    for (int32_t e = rb; e < re; ++e) {  // the whole row, so both halves decide alike
-      const int32_t f = it.cols[e];
-      if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
+    // over the whole walk (both rows, every entry), so that both halves of
+    // a split item decide alike
+    for (int r = 0; r < (two ? 2 : 1); ++r) {
+      const RowCursor c = row_cursor(a, r ? wi.t1 : wi.t0);
+      for (int32_t e = c.e; e < c.e_end; ++e) {
+        const int32_t f = c.cols[e];
+        if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
+      }
     }
     float ss = 0.f;  // |q'_i|^2 of the scaled, rounded rows
 #pragma unroll
@@ -609,24 +715,27 @@ void lvsa_attn_fwd(Args a) {
   // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
   // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
   // barrier per tile.  Unrolled by two so that every LDS offset is an
-  // immediate.
-  int pos = 0, kv = 0;
-  auto advance = [&]() {  // next tile, moving to the next run when needed
+  // immediate.  A tile is computed by the waves whose rows attend its frame
+  // (every wave, unless the tile's rows cross a frame boundary).
+  int pos = 0, kv = 0, mem = 0;
+  auto advance = [&]() {  // next tile, moving to the next segment when needed
     pos += C::BN;
     if (pos >= it.ke) {
-      it.next_run();
+      it.next();
       pos = it.ks;
     }
     kv = min(C::BN, it.ke - pos);
+    mem = it.mem;
   };
   auto issue = [&](int buf) {
     blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
     blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
   };
   if (n_walk > 0) {
-    it.next_run();
+    it.next();
     pos = it.ks;
     kv = min(C::BN, it.ke - pos);
+    mem = it.mem;
     issue(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -635,23 +744,31 @@ void lvsa_attn_fwd(Args a) {
   // workgroup runs the same loads and barriers in either.
   auto run = [&](auto fixed_c) {
     constexpr bool F = decltype(fixed_c)::value;
+    auto step = [&](auto buf_c, int kvj, int memj) {
+      constexpr int BUF = decltype(buf_c)::value;
+      if (compute && (memj & need)) {
+        // a boundary-crossing wave, on a frame only one of its two frames attends
+        const bool lm = need == 3 && memj != 3;
+        blk.template tile<BUF, F>(kvj, lm, memj == 2 ? lanes_t1 : ~lanes_t1);
+      }
+    };
     for (int i = 0; i + 1 < n_walk; i += 2) {
-      const int kv0 = kv;
+      const int kv0 = kv, mem0 = mem;
       advance();  // tile i+1 -> buffer 1
       issue(1);
-      if (compute) blk.template tile<0, F>(kv0);
+      step(std::integral_constant<int, 0>{}, kv0, mem0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      const int kv1 = kv;
+      const int kv1 = kv, mem1 = mem;
       if (i + 2 < n_walk) {  // tile i+2 -> buffer 0
         advance();
         issue(0);
       }
-      if (compute) blk.template tile<1, F>(kv1);
+      step(std::integral_constant<int, 1>{}, kv1, mem1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if ((n_walk & 1) && compute) blk.template tile<0, F>(kv);
+    if (n_walk & 1) step(std::integral_constant<int, 0>{}, kv, mem);
   };
   if (fixed)
     run(std::true_type{});
@@ -678,12 +795,11 @@ void lvsa_attn_fwd(Args a) {
 
   // ---- epilogue: normalise, round to bf16, store
   {
-    const int r = row0 + blk.l32;
     // both lane halves hold the same row: reduce before the early exit
     const float l_tot = swap_halves_sum(blk.l_run);
-    if (r < P) {
+    if (my_row < wi.tok_end) {
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-      u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * P + r) * a.o_sn;
+      u16 *op = a.o + (int64_t)wi.b * a.o_sb + (int64_t)wi.h * a.o_sh + (int64_t)my_row * a.o_sn;
 #pragma unroll
       for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
@@ -740,38 +856,34 @@ __global__ __launch_bounds__(256) void lvsa_key_norms(const u16 *k, int64_t k_sb
 // query), rescales both to the larger reference, adds, normalises and
 // stores the item's output rows.  Runs after lvsa_attn_fwd on the same
 // stream, so the records are complete.
-template <int D, int NW>
+template <int D, int NW, bool SPAN>
 __global__ __launch_bounds__(NW * 64) void lvsa_combine(Args a) {
   const int x = blockIdx.x / a.split_cap, j = blockIdx.x % a.split_cap;
   int base, cnt;
   xcd_range(a.n_wg, x, &base, &cnt);
   const int S = split_count(a.split_cap, cnt);
   if (j >= S) return;
-  const int item = base + (cnt - S) + j;
-  const int qt = item % a.q_tiles;
-  const int rest = item / a.q_tiles;
-  const int t = rest % a.T;
-  const int bh = rest / a.T;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
+  const Item wi = decode_item<NW * 32, SPAN>(a, base + (cnt - S) + j);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = qt * NW * 32 + wave * 32;
-  if (row0 >= a.P) return;  // a wave with no rows wrote no record
+  const int row0 = wi.tok0 + wave * 32;
+  if (row0 >= wi.tok_end) return;  // a wave with no rows wrote no record
   constexpr int R4 = kPartialFloats(D) / 4;
   const float4 *r0 = reinterpret_cast<const float4 *>(a.partial) + ((int64_t)(blockIdx.x * 2) * NW + wave) * R4 * 64 + lane;
   const float4 *r1 = r0 + (int64_t)NW * R4 * 64;
   const float4 t0 = r0[(R4 - 1) * 64], t1 = r1[(R4 - 1) * 64];
-  // weights 2^(m_h - m); a half that saw no key has m_h = -inf and weight 0
+  // weights 2^(m_h - m); a half that saw no key of a row has l_h = 0 and
+  // m_h = -FLT_MAX (its start), so its weight is 0 unless neither half saw
+  // one (then l = 0 and the row is zero)
   const float m = fmaxf(t0.y, t1.y);
-  const float w0 = t0.y == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t0.y - m);
-  const float w1 = t1.y == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(t1.y - m);
+  const float w0 = __builtin_amdgcn_exp2f(t0.y - m);
+  const float w1 = __builtin_amdgcn_exp2f(t1.y - m);
   const float l = w0 * t0.x + w1 * t1.x;
   const float l_tot = swap_halves_sum(l);
   const int r = row0 + (lane & 31);
-  if (r >= a.P) return;
+  if (r >= wi.tok_end) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  u16 *op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + ((int64_t)t * a.P + r) * a.o_sn;
+  u16 *op = a.o + (int64_t)wi.b * a.o_sb + (int64_t)wi.h * a.o_sh + (int64_t)r * a.o_sn;
 #pragma unroll
   for (int dc = 0; dc < D / 32; ++dc)
 #pragma unroll
@@ -886,12 +998,12 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
   return a0 < b1 && b0 < a1;
 }
 
-template <int D, int NW>
-int launch(const Args &args, hipStream_t stream) {
+template <int D, int NW, bool SPAN>
+int launch(const Args &args, int n_frames, hipStream_t stream) {
   if (args.knorm) {
     // the key-norm table first, on the same stream
-    hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(args.n_wg / args.q_tiles), dim3(256), 0, stream, args.k, args.k_sb,
-                       args.k_sh, args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.knorm), args.tickets);
+    hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(n_frames), dim3(256), 0, stream, args.k, args.k_sb, args.k_sh,
+                       args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.knorm), args.tickets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "key-norm kernel launch failed: %s", hipGetErrorString(e));
   }
@@ -900,38 +1012,70 @@ int launch(const Args &args, hipStream_t stream) {
   // share of the others' items.
   const int64_t grid =
       args.tickets ? args.n_wg + (int64_t)kNumXcd * args.split_cap + args.n_wg / 8 + kNumXcd : args.n_wg;
-  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW, SPAN>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (args.tickets && args.split_cap > 0) {
-    hipLaunchKernelGGL((lvsa_combine<D, NW>), dim3(kNumXcd * args.split_cap), dim3(NW * 64), 0, stream, args);
+    hipLaunchKernelGGL((lvsa_combine<D, NW, SPAN>), dim3(kNumXcd * args.split_cap), dim3(NW * 64), 0, stream, args);
     e = hipGetLastError();
     if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
   }
   return lvsa::ok();
 }
 
+// How a call is cut into work items.  Frames of at least kSpanRows tokens
+// (every video workload) use 12-wave workgroups of kSpanRows consecutive
+// tokens, which may cross one frame boundary; one such workgroup fills a
+// CU (3 waves per SIMD) and loads each K/V tile once for three times the
+// rows of a 4-wave one.  Shorter frames use 4-wave workgroups of 128 rows
+// of one frame.
+constexpr int kSpanWaves = 12;
+constexpr int kSpanRows = kSpanWaves * 32;
+constexpr int kFrameWaves = 4;
+struct Plan {
+  bool span;
+  int nw, q_tiles;
+  int64_t items;
+  int32_t split_per_xcd;  // items per XCD range run as two halves, at most
+};
+Plan plan_for(int64_t B, int64_t H, int64_t N, int64_t T) {
+  Plan p;
+  const int64_t P = N / T;
+  p.span = P >= kSpanRows;
+  if (p.span) {
+    p.nw = kSpanWaves;
+    p.q_tiles = (int)((N + kSpanRows - 1) / kSpanRows);
+    p.items = B * H * p.q_tiles;
+    p.split_per_xcd = 32;
+  } else {
+    p.nw = kFrameWaves;
+    p.q_tiles = (int)((P + kFrameWaves * 32 - 1) / (kFrameWaves * 32));
+    p.items = B * H * T * p.q_tiles;
+    p.split_per_xcd = 96;
+  }
+  return p;
+}
+
 // Workspace: the key-norm table (B·H·T floats), then, at the next
 // 256-byte boundary, the 8 ticket counters (256 bytes), then the partial
 // records of the split items (8·split_cap slots × 2 halves × NW waves × 64
 // lanes × kPartialFloats(D) floats).
-constexpr int kSplitPerXcd = 96;  // items per XCD range run as two halves, at most
 int64_t norms_bytes_for(int64_t B, int64_t H, int64_t T) {
   return ((B * H * T * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
-int64_t items_for(int64_t B, int64_t H, int64_t N, int64_t T) {
-  const int64_t P = N / T, BM = LVSA_NW * 32;
-  return B * H * T * ((P + BM - 1) / BM);
-}
 // At most a quarter of every XCD range is split.
-int32_t split_cap_for(int64_t items) { return (int32_t)std::min<int64_t>(kSplitPerXcd, items / (4 * kNumXcd)); }
+int32_t split_cap_for(const Plan &p) {
+  return (int32_t)std::min<int64_t>(p.split_per_xcd, p.items / (4 * kNumXcd));
+}
 // Bytes of partial records per unit of split_cap (one slot per XCD).
-int64_t split_unit_bytes(int64_t D) { return (int64_t)kNumXcd * 2 * LVSA_NW * 64 * kPartialFloats((int)D) * 4; }
+int64_t split_unit_bytes(const Plan &p, int64_t D) {
+  return (int64_t)kNumXcd * 2 * p.nw * 64 * kPartialFloats((int)D) * 4;
+}
 int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T, int32_t split_cap) {
-  return norms_bytes_for(B, H, T) + 256 + split_cap * split_unit_bytes(D);
+  return norms_bytes_for(B, H, T) + 256 + split_cap * split_unit_bytes(plan_for(B, H, N, T), D);
 }
 int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T) {
-  return workspace_bytes_for(B, H, N, D, T, split_cap_for(items_for(B, H, N, T)));
+  return workspace_bytes_for(B, H, N, D, T, split_cap_for(plan_for(B, H, N, T)));
 }
 
 int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor *v,
@@ -961,7 +1105,7 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   }
   int32_t split_cap = 0;
   if (use_ws) {
-    split_cap = split_cap_for(items_for(q->B, q->H, q->N, T));
+    split_cap = split_cap_for(plan_for(q->B, q->H, q->N, T));
     if (split_cap_limit >= 0) split_cap = std::min(split_cap, split_cap_limit);
     const int64_t need = workspace_bytes_for(q->B, q->H, q->N, q->D, T, split_cap);
     if (!workspace) return lvsa::fail(LVSA_ERR_ARG, "workspace is NULL");
@@ -982,10 +1126,9 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
 
   const int D = (int)q->D;
   const int P = (int)(q->N / T);
-  constexpr int NW = LVSA_NW;
-  const int BM = NW * 32;
-  const int q_tiles = (P + BM - 1) / BM;
-  const int64_t n_wg = (int64_t)q->B * q->H * T * q_tiles;
+  const Plan plan = plan_for(q->B, q->H, q->N, T);
+  const int q_tiles = plan.q_tiles;
+  const int64_t n_wg = plan.items;
   if (n_wg > INT32_MAX / 2) return lvsa::fail(LVSA_ERR_SHAPE, "grid of %lld workgroups too large", (long long)n_wg);
 
   Args a;
@@ -1015,8 +1158,13 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   a.split_cap = split_cap;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128) return launch<128, NW>(a, s);
-  return launch<64, NW>(a, s);
+  const int n_frames = (int)(q->B * q->H * T);
+  if (plan.span) {
+    if (D == 128) return launch<128, kSpanWaves, true>(a, n_frames, s);
+    return launch<64, kSpanWaves, true>(a, n_frames, s);
+  }
+  if (D == 128) return launch<128, kFrameWaves, false>(a, n_frames, s);
+  return launch<64, kFrameWaves, false>(a, n_frames, s);
 }
 
 }  // namespace
@@ -1068,7 +1216,8 @@ extern "C" int lvsa_attention_ws_static(const lvsa_tensor *q, const lvsa_tensor 
   void *ws;
   if ((rc = static_scratch_ptr(dev, &ws))) return rc;
   const int64_t fixed = norms_bytes_for(q->B, q->H, T) + 256;
-  const int32_t cap = (int32_t)std::min<int64_t>(INT32_MAX, (kStaticScratchBytes - fixed) / split_unit_bytes(q->D));
+  const int32_t cap = (int32_t)std::min<int64_t>(
+      INT32_MAX, (kStaticScratchBytes - fixed) / split_unit_bytes(plan_for(q->B, q->H, q->N, T), q->D));
   return attention_impl(q, k, v, row_ptr_dev, col_idx_dev, T, nnz, out, scale, ws, kStaticScratchBytes, true,
                         stream, cap);
 }

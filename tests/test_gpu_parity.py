@@ -88,6 +88,12 @@ MID_CASES = [
     (2, 2, 7, 129, 64, 7, 3, 105),     # C = T: dense, one run of 903 keys; 1-row last tile
     (1, 1, 1, 300, 128, 4, 2, 106),    # a single frame
     (1, 3, 20, 64, 128, 9, 4, 107),    # key tiles exactly aligned to frames
+    # frames of >= 384 tokens: 12-wave items of 384 consecutive tokens, which
+    # cross frame boundaries and walk the union of two frames' rows
+    (1, 2, 7, 400, 128, 4, 2, 108),    # nearly every item crosses a boundary (inside a wave)
+    (2, 1, 5, 384, 64, 3, 1, 109),     # items aligned to frames: none crosses
+    (1, 3, 6, 1000, 64, 4, 2, 110),    # d = 64, a boundary inside a wave
+    (1, 1, 3, 777, 128, 2, 1, 111),    # C = 2: one anchor, one window frame
 ]
 
 
@@ -163,10 +169,13 @@ def test_shared_kv_heads_by_zero_stride(gpu):
     check_key_norms(ws, k1.expand(B, H, T * P, d), T)
 
 
-def test_custom_csr_masks(gpu):
+@pytest.mark.parametrize("P", [150, 430])
+def test_custom_csr_masks(gpu, P):
     # Variable-length, non-LVSA rows (window-only / anchor-only ablations use
-    # the same kernel): the kernel follows any ascending CSR row.
-    B, H, T, P, d = 1, 2, 11, 150, 128
+    # the same kernel): the kernel follows any ascending CSR row.  At P = 430
+    # the work items cross frame boundaries and walk the union of two
+    # unrelated rows.
+    B, H, T, d = 1, 2, 11, 128
     say("custom csr", (B, H, T, P, d))
     q = make_random((B, H, T * P, d), 301)
     k = make_random((B, H, T * P, d), 302)
@@ -199,10 +208,13 @@ def kept_entries(row, T):
     return out
 
 
-def test_malformed_mask_entries_are_skipped_and_empty_rows_give_zeros(gpu):
+@pytest.mark.parametrize("P", [150, 400])
+def test_malformed_mask_entries_are_skipped_and_empty_rows_give_zeros(gpu, P):
     # Out-of-range, empty, descending and repeated entries; P = 150 gives a
-    # full and a partial query tile per frame.
-    B, H, T, P, d = 1, 1, 8, 150, 64
+    # full and a partial query tile per frame; at P = 400 the work items
+    # cross frame boundaries (an empty row next to a non-empty one, malformed
+    # rows merged with their neighbours).
+    B, H, T, d = 1, 1, 8, 64
     say("malformed mask", (B, H, T, P, d))
     q = make_random((B, H, T * P, d), 401)
     k = make_random((B, H, T * P, d), 402)
@@ -381,16 +393,20 @@ def test_workspace_takes_a_fixed_reference_and_falls_back_on_large_norms(gpu):
     assert_close(a[0, 0, toks], oa.block_attention_rows(q, k, v_big, rows, 0, 0, toks), "large values")
 
 
+@pytest.mark.parametrize("P", [150, 400])
 @pytest.mark.parametrize("tail_rows", [([5], []), ([3, 1, 3, 4], [2, 2, 0, 7, 6])], ids=["single-and-empty", "malformed"])
-def test_workspace_split_items_merge_their_halves(gpu, tail_rows):
+def test_workspace_split_items_merge_their_halves(gpu, tail_rows, P):
     # With a workspace, the last items of each XCD range run as two halves of
-    # their CSR row, merged afterwards.  Here 8 heads x 8 frames x 2 query
+    # their walk, merged afterwards.  P = 150: 8 heads x 8 frames x 2 query
     # tiles = 128 items, 16 per range: each range is one head, and its last 4
-    # items (frames 6 and 7) are split.  Those rows are a single entry (the
-    # first half sees no key), an empty row (neither does), or malformed
-    # rows whose skipped entries straddle the split point.  Every output row
-    # must match the oracle on the kept entries; empty rows give zeros.
-    B, H, T, P, d = 1, 8, 8, 150, 64
+    # items (frames 6 and 7) are split.  P = 400: 8 heads x 9 items of 384
+    # tokens, one head per range, its last 2 items split: tokens 2688-3071
+    # (frames 6 and 7, the union of both rows) and 3072-3199 (frame 7).
+    # Those rows are a single entry (the first half sees no key), an empty
+    # row (neither does), or malformed rows whose skipped entries straddle
+    # the split point.  Every output row must match the oracle on the kept
+    # entries; empty rows give zeros.
+    B, H, T, d = 1, 8, 8, 64
     say("workspace split halves", (B, H, T, P, d), tail_rows)
     q = make_random((B, H, T * P, d), 411)
     k = make_random((B, H, T * P, d), 412)
@@ -456,14 +472,20 @@ FULL = [
 
 
 def sample_tokens(T, P, rnd, n_rand=12):
-    """Structured tokens (frame starts and ends, 128-row query-tile edges, the
-    first row of a frame's partial last tile) of four frames, plus random ones."""
+    """Structured tokens of four frames -- frame starts and ends, 128-row
+    query-tile edges, the first row of a frame's partial last 128-row tile,
+    and the edges of the 384-token work items that cross into the frame --
+    plus random ones."""
     last_tile = (P // 128) * 128
     toks = set()
     for t in (0, 1, T // 2, T - 1):
         for p in (0, 1, 127, 128, 255, 256, last_tile - 1, last_tile, P - 25, P - 24, P - 1):
             if 0 <= p < P:
                 toks.add(t * P + p)
+        edge = -(-t * P // 384) * 384  # first 384-token item boundary at or after the frame start
+        while edge < (t + 1) * P and len(toks) < 400:
+            toks.update(x for x in (edge - 1, edge, edge + 31, edge + 32) if t * P <= x < (t + 1) * P)
+            edge += 384
     n_structured = len(toks)
     while len(toks) < n_structured + n_rand:
         toks.add(rnd.randrange(T * P))
@@ -522,27 +544,41 @@ def test_dense_mask_at_full_size_sampled(gpu):
 
 # ---------------- the workspace path at full size: every workload, split items --
 
-BM = 128     # query rows per work item (4 waves x 32 rows)
 N_XCD = 8    # XCDs of the part, one contiguous item range each
-SPLIT_PER_XCD = 96
+
+
+def work_plan(B, H, T, P):
+    """How lvsa_attention_ws cuts a call into work items, as include/lvsa.h
+    states it: frames of at least 384 tokens give items of 384 consecutive
+    tokens of one (b, h), ordered (b, h, tile), of which at most 32 per XCD
+    range are split; shorter frames give items of 128 rows of one frame,
+    ordered (b, h, frame, tile), at most 96 split per range.  Returns
+    (rows per item, tiles per unit, item count, split items per range)."""
+    N = T * P
+    if P >= 384:
+        q_tiles = (N + 383) // 384
+        return 384, q_tiles, B * H * q_tiles, 32
+    q_tiles = (P + 127) // 128
+    return 128, q_tiles, B * H * T * q_tiles, 96
 
 
 def split_layout(B, H, T, P):
-    """Work items of lvsa_attention_ws, as include/lvsa.h states them: items
-    (b, h, frame, query tile) in that order (query tile fastest) are cut into
-    8 contiguous ranges, and the last min(96, items/32, range/4) items of each
-    range run as two halves merged afterwards.  Returns, per range, the
-    (b, h, t, query tile) of its first split item, its last item and the last
-    item it runs whole (None where a range has no such item)."""
-    q_tiles = (P + BM - 1) // BM
-    n = B * H * T * q_tiles
-    cap = min(SPLIT_PER_XCD, n // (4 * N_XCD))
+    """The 8 contiguous item ranges, one per XCD, and the last
+    min(cap, items/32, range/4) items of each, run as two halves merged
+    afterwards.  Returns, per range, (b, h, first token, end token) of its
+    first split item, its last item and the last item it runs whole (None
+    where a range has no such item)."""
+    bm, q_tiles, n, split = work_plan(B, H, T, P)
+    cap = min(split, n // (4 * N_XCD))
     per, rem = divmod(n, N_XCD)
 
     def decode(item):
         qt, rest = item % q_tiles, item // q_tiles
+        if bm == 384:
+            b, h = rest // H, rest % H
+            return b, h, qt * 384, min(T * P, qt * 384 + 384)
         t, bh = rest % T, rest // T
-        return bh // H, bh % H, t, qt
+        return bh // H, bh % H, t * P + qt * 128, min((t + 1) * P, t * P + qt * 128 + 128)
 
     out = []
     for x in range(N_XCD):
@@ -556,15 +592,12 @@ def split_layout(B, H, T, P):
     return out
 
 
-def item_rows(t, qt, P):
-    """The first and last row of each wave of a query tile (frame-relative
-    rows -> tokens)."""
+def item_rows(tok0, tok_end):
+    """The first and last row of each wave of a work item, as tokens."""
     rows = set()
-    for w in range(BM // 32):
-        for r in (w * 32, w * 32 + 31):
-            p = qt * BM + r
-            if p < P:
-                rows.add(t * P + p)
+    for w0 in range(tok0, tok_end, 32):
+        rows.add(w0)
+        rows.add(min(w0 + 31, tok_end - 1))
     return rows
 
 
@@ -625,8 +658,8 @@ def test_workspace_full_size_sampled(gpu, name, steps, flag_list):
             for h in (0, w.H - 1):
                 samples.setdefault((0, h), set()).update(toks)
             for item in (it for rng in layout for it in rng if it is not None):
-                b, h, t, qt = item
-                samples.setdefault((b, h), set()).update(item_rows(t, qt, w.P))
+                b, h, tok0, tok_end = item
+                samples.setdefault((b, h), set()).update(item_rows(tok0, tok_end))
             check_sampled(out, heads, rows, samples, f"ws {name} step {s} flags {flags}")
 
 
