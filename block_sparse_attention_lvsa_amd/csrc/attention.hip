@@ -131,30 +131,6 @@ struct Args {
 typedef const __attribute__((address_space(4))) int32_t *const_i32p;
 typedef const __attribute__((address_space(4))) float *const_f32p;
 
-// One CSR row's entries, in order.  An entry outside [0, T), or not above
-// the last entry taken, is skipped, so a malformed row never causes an
-// out-of-range read and never repeats a frame.  Every value is wave-uniform
-// (scalar registers).
-struct RowCursor {
-  const_i32p cols;
-  int32_t e, e_end, T;
-  int32_t last;  // last frame taken (-1 before the first)
-
-  // The next frame the row keeps, or T when it has none left.
-  __device__ int32_t peek() {
-    while (e < e_end) {
-      const int32_t f = cols[e];
-      if (f > last && f < T) return f;
-      ++e;
-    }
-    return T;
-  }
-  __device__ void take(int32_t f) {
-    last = f;
-    ++e;
-  }
-};
-
 // The key walk of a workgroup whose query rows lie in frames t0 and t1
 // (t1 = t0, or t0 + 1 when the rows cross a frame boundary): the union of
 // the two CSR rows, in ascending frame order, as segments of consecutive
@@ -162,37 +138,68 @@ struct RowCursor {
 // A(t1); with one row both bits are set).  Tokens are frame-major, so a
 // segment of frames [f0, f1] is the one contiguous token range
 // [f0·P, (f1+1)·P).  Frames at or above f_hi are not walked.
+//
+// Each row's entries are read in order; an entry outside [0, T), or not
+// above the last entry taken from its row, is skipped, so a malformed row
+// never causes an out-of-range read and never repeats a frame.  Every value
+// is wave-uniform (scalar registers; the state is kept small, since the
+// main loop's scalar registers are scarce).
 struct SegIter {
-  RowCursor r0, r1;
-  int32_t f_hi, P;
-  bool two;
+  const_i32p cols;
+  int32_t T, P, f_hi;
+  int32_t e0, end0, last0;  // row of t0: next entry, end, last frame taken
+  int32_t e1, end1, last1;  // row of t1 (no entries when the walk has one row)
+  int32_t bits0;            // membership of a frame of row t0: 1, or 3 with one row
   int32_t ks, ke, mem;
 
-  __device__ int32_t peek1() { return two ? r1.peek() : r0.T; }
-  __device__ int members(int32_t f, int32_t a0, int32_t a1) const {
-    return two ? ((a0 == f ? 1 : 0) | (a1 == f ? 2 : 0)) : (a0 == f ? 3 : 0);
+  // The next frame row 0 (row 1) keeps, or T when it has none left.
+  __device__ int32_t peek0() {
+    while (e0 < end0) {
+      const int32_t f = cols[e0];
+      if (f > last0 && f < T) return f;
+      ++e0;
+    }
+    return T;
   }
-  __device__ void take(int32_t f, int32_t a0, int32_t a1) {
-    if (a0 == f) r0.take(f);
-    if (two && a1 == f) r1.take(f);
+  __device__ int32_t peek1() {
+    while (e1 < end1) {
+      const int32_t f = cols[e1];
+      if (f > last1 && f < T) return f;
+      ++e1;
+    }
+    return T;
+  }
+  // Takes frame f from the rows whose next frame it is; returns its membership.
+  __device__ int take(int32_t f, int32_t a0, int32_t a1) {
+    int m = 0;
+    if (a0 == f) {
+      last0 = f;
+      ++e0;
+      m = bits0;
+    }
+    if (a1 == f) {
+      last1 = f;
+      ++e1;
+      m |= 2;
+    }
+    return m;
   }
   // Skips every frame below f_lo (the second half of a split walk).
   __device__ void skip_below(int32_t f_lo) {
-    while (r0.peek() < f_lo) r0.take(r0.peek());
-    if (two)
-      while (r1.peek() < f_lo) r1.take(r1.peek());
+    for (int32_t f; (f = peek0()) < f_lo;) take(f, f, T);
+    for (int32_t f; (f = peek1()) < f_lo;) take(f, T, f);
   }
   __device__ bool next() {
-    int32_t a0 = r0.peek(), a1 = peek1();
+    int32_t a0 = peek0(), a1 = peek1();
     const int32_t fs = min(a0, a1);
     if (fs >= f_hi) return false;
-    const int m = members(fs, a0, a1);
-    take(fs, a0, a1);
+    const int m = take(fs, a0, a1);
     int32_t fe = fs;
     while (fe + 1 < f_hi) {
-      a0 = r0.peek();
+      a0 = peek0();
       a1 = peek1();
-      if (members(fe + 1, a0, a1) != m) break;
+      const int mm = (a0 == fe + 1 ? bits0 : 0) | (a1 == fe + 1 ? 2 : 0);
+      if (mm != m) break;
       take(fe + 1, a0, a1);
       ++fe;
     }
@@ -508,19 +515,14 @@ __device__ __forceinline__ Item decode_item(const Args &a, int item) {
   return it;
 }
 
-// CSR row t, its offsets clamped to [0, nnz].
-__device__ __forceinline__ RowCursor row_cursor(const Args &a, int t) {
+// The entries [rb, re) of CSR row t, offsets clamped to [0, nnz].
+__device__ __forceinline__ void row_range(const Args &a, int t, int32_t *rb, int32_t *re) {
   const const_i32p rp = (const_i32p)a.row_ptr;
-  int32_t rb = rp[t], re = rp[t + 1];
-  rb = rb < 0 ? 0 : (rb > a.nnz ? a.nnz : rb);
-  re = re < rb ? rb : (re > a.nnz ? a.nnz : re);
-  RowCursor c;
-  c.cols = (const_i32p)a.col_idx;
-  c.e = rb;
-  c.e_end = re;
-  c.T = a.T;
-  c.last = -1;
-  return c;
+  int32_t b = rp[t], e = rp[t + 1];
+  b = b < 0 ? 0 : (b > a.nnz ? a.nnz : b);
+  e = e < b ? b : (e > a.nnz ? a.nnz : e);
+  *rb = b;
+  *re = e;
 }
 
 template <int D, int NW, bool SPAN>
@@ -644,18 +646,23 @@ void lvsa_attn_fwd(Args a) {
   // below fm, the second the rest, so that together they walk exactly what
   // the whole walk does)
   SegIter it;
-  it.r0 = row_cursor(a, wi.t0);
-  it.r1 = two ? row_cursor(a, wi.t1) : it.r0;
-  it.two = two;
+  it.cols = (const_i32p)a.col_idx;
+  it.T = a.T;
   it.P = P;
   it.f_hi = a.T;
+  row_range(a, wi.t0, &it.e0, &it.end0);
+  if (two)
+    row_range(a, wi.t1, &it.e1, &it.end1);
+  else
+    it.e1 = it.end1 = 0;
+  it.last0 = it.last1 = -1;
+  it.bits0 = two ? 1 : 3;
   it.ks = it.ke = it.mem = 0;
   if (half >= 0) {
     // fm: the middle entry of t0's row (any frame partitions the walk; the
     // middle one halves it for well-formed rows)
-    const int32_t rb0 = it.r0.e, re0 = it.r0.e_end;
-    const int32_t mid = rb0 + (re0 - rb0) / 2;
-    int32_t fm = re0 > rb0 ? it.r0.cols[mid] : 0;
+    const int32_t mid = it.e0 + (it.end0 - it.e0) / 2;
+    int32_t fm = it.end0 > it.e0 ? it.cols[mid] : 0;
     fm = fm < 0 ? 0 : (fm > a.T ? a.T : fm);
     if (half == 0)
       it.f_hi = fm;
@@ -684,9 +691,10 @@ void lvsa_attn_fwd(Args a) {
     // over the whole walk (both rows, every entry), so that both halves of
     // a split item decide alike
     for (int r = 0; r < (two ? 2 : 1); ++r) {
-      const RowCursor c = row_cursor(a, r ? wi.t1 : wi.t0);
-      for (int32_t e = c.e; e < c.e_end; ++e) {
-        const int32_t f = c.cols[e];
+      int32_t rb, re;
+      row_range(a, r ? wi.t1 : wi.t0, &rb, &re);
+      for (int32_t e = rb; e < re; ++e) {
+        const int32_t f = it.cols[e];
         if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
       }
     }
@@ -948,12 +956,19 @@ int check_tensor(const lvsa_tensor *x, const char *name) {
   if (!x || !x->data) return lvsa::fail(LVSA_ERR_ARG, "%s: NULL tensor or data pointer", name);
   if (x->dtype != LVSA_DTYPE_BF16) return lvsa::fail(LVSA_ERR_DTYPE, "%s: dtype %d, only bf16 is supported", name, x->dtype);
   if (x->B < 1 || x->H < 1 || x->N < 1) return lvsa::fail(LVSA_ERR_SHAPE, "%s: empty or negative B/H/N", name);
+  if (x->B > INT32_MAX || x->H > INT32_MAX || x->N > INT32_MAX)
+    return lvsa::fail(LVSA_ERR_SHAPE, "%s: B/H/N above 2^31", name);
   if (x->D != 64 && x->D != 128) return lvsa::fail(LVSA_ERR_SHAPE, "%s: D=%lld, supported 64 and 128", name, (long long)x->D);
   if (reinterpret_cast<uintptr_t>(x->data) % 16) return lvsa::fail(LVSA_ERR_SHAPE, "%s: data not 16-byte aligned", name);
   if (x->stride_n < x->D || x->stride_b < 0 || x->stride_h < 0 || x->stride_n % 8 || x->stride_h % 8 || x->stride_b % 8)
     return lvsa::fail(LVSA_ERR_SHAPE, "%s: strides must be multiples of 8 elements with stride_n >= D", name);
   if (x->stride_n > (int64_t{1} << 24))
     return lvsa::fail(LVSA_ERR_SHAPE, "%s: stride_n above 2^24 elements is not supported", name);
+  // byte extent, in floating point first so that the int64 arithmetic below
+  // and in extent() cannot overflow
+  const double span = (double)(x->B - 1) * (double)x->stride_b + (double)(x->H - 1) * (double)x->stride_h +
+                      (double)(x->N - 1) * (double)x->stride_n + (double)x->D;
+  if (span * 2.0 > 0x1p62) return lvsa::fail(LVSA_ERR_SHAPE, "%s: strides span more than 2^62 bytes", name);
   return LVSA_OK;
 }
 
@@ -1046,7 +1061,7 @@ Plan plan_for(int64_t B, int64_t H, int64_t N, int64_t T) {
     p.nw = kSpanWaves;
     p.q_tiles = (int)((N + kSpanRows - 1) / kSpanRows);
     p.items = B * H * p.q_tiles;
-    p.split_per_xcd = 32;
+    p.split_per_xcd = 32;  // 16-128 measured within 0.8% of each other; 32 best or tied
   } else {
     p.nw = kFrameWaves;
     p.q_tiles = (int)((P + kFrameWaves * 32 - 1) / (kFrameWaves * 32));
@@ -1096,6 +1111,8 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   if (T < 1) return lvsa::fail(LVSA_ERR_ARG, "T=%d: need T >= 1", T);
   if (q->N % T) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld is not a multiple of T=%d", (long long)q->N, T);
   if (q->N > INT32_MAX / 2) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld too large", (long long)q->N);
+  if ((double)q->B * (double)q->H * (double)q->N > 0x1p46)
+    return lvsa::fail(LVSA_ERR_SHAPE, "B*H*N = %.3g tokens too large", (double)q->B * (double)q->H * (double)q->N);
   if (!row_ptr_dev || !col_idx_dev || nnz < 0)
     return lvsa::fail(LVSA_ERR_ARG, "row_ptr/col_idx NULL or nnz < 0");
   {
@@ -1182,7 +1199,7 @@ extern "C" int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, i
   if (B < 1 || H < 1 || T < 1 || N < 1) return lvsa::fail(LVSA_ERR_ARG, "B, H, N and T must be >= 1");
   if (D != 64 && D != 128) return lvsa::fail(LVSA_ERR_SHAPE, "D=%lld, supported 64 and 128", (long long)D);
   if (N % T) return lvsa::fail(LVSA_ERR_SHAPE, "N=%lld is not a multiple of T=%d", (long long)N, T);
-  if (N > INT32_MAX / 2 || B * H > (int64_t{1} << 40) / N)
+  if (N > INT32_MAX / 2 || (double)B * (double)H * (double)N > 0x1p40)
     return lvsa::fail(LVSA_ERR_ARG, "B*H*N too large");
   *bytes = workspace_bytes_for(B, H, N, D, T);
   return lvsa::ok();
