@@ -15,8 +15,13 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   value         effective TFLOP/s = algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d
                 per step ÷ time per step (padding and softmax not counted)
   roofline      the attention kernel: HIP events around each launch on its
-                stream; HBM bytes from the committed rocprofv3 summary
-  cpu_baseline  the float64 CPU oracle on a bounded sample of the same step
+                stream, against the vendor bf16 peak and against the peak a
+                matrix-core microbenchmark measures on this GPU
+                (libmfma_peak.so); the L2-to-fabric bytes per launch from the
+                committed rocprofv3 counter summary (null once the kernel
+                source differs from the one the counters were taken on)
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same step,
+                and the pure-Python oracle mask builder per step
   also          per-call kernel median/p10/p90, host mask build and mask H2D
                 times, dense comparator (same kernel, C = T mask) and speedup,
                 peak device memory; an outside reference (torch SDPA, flash
@@ -27,6 +32,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload wan13b_6x]
     python bench.py --sweep [--sweep-out FILE]   # every workload, table on stderr
+    python bench.py --library OTHER/liblvsa.so   # time another build (A/B)
 """
 
 from __future__ import annotations
@@ -43,8 +49,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure (2.4 GHz engine clock)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, vendor figure
 METRIC = "LVSA attention effective TFLOP/s + ms/call, T=121×1560 tok, H=12 d=128 bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_wan13b_6x.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_lvsa_amd", "csrc", "attention.hip")]
@@ -68,7 +74,8 @@ def algorithmic_flops(w) -> float:
 
 
 def measured_traffic(w):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
+    """The committed rocprofv3 counter record of the attention kernel
+    (L2-to-fabric bytes per launch and their spread over launches), or None
     when it is missing or was taken on a different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -77,15 +84,37 @@ def measured_traffic(w):
         return None
     if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != w.name:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def mfma_peak_probe(seconds=0.5):
+    """Sustained dense bf16 MFMA rate of this GPU (TFLOP/s) and its engine
+    clock (MHz), from libmfma_peak.so; (None, None) if it is not built."""
+    path = os.path.join(ROOT, "block_sparse_attention_lvsa_amd", "libmfma_peak.so")
+    if not os.path.exists(path):
+        return None, None
+    lib = ctypes.CDLL(path)
+    lib.lvsa_probe_mfma_peak.restype = ctypes.c_int
+    lib.lvsa_probe_mfma_peak.argtypes = [ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double)]
+    tf, mhz = ctypes.c_double(0), ctypes.c_double(0)
+    if lib.lvsa_probe_mfma_peak(seconds, ctypes.byref(tf), ctypes.byref(mhz)) != 0:
+        return None, None
+    return tf.value, mhz.value
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
     """The float64 oracle on a bounded sample: query frames of head 0 at step
-    0, taken in order until ``budget_s`` of CPU time is used."""
+    0, taken in order until ``budget_s`` of CPU time is used.  Also times the
+    pure-Python oracle mask builder per step (steps 0..49), beside the C++
+    builder's time the GPU leg reports."""
     import torch
     import oracle
 
+    m0 = time.perf_counter()
+    for s in range(50):
+        oracle.build_mask(w.T, w.C, w.W, s)
+    mask_us = (time.perf_counter() - m0) / 50 * 1e6
     rows = oracle.key_frames(w.T, w.C, w.W, 0)
     qh, kh, vh = (x[:, :1].cpu() for x in (q, k, v))
     threads = torch.get_num_threads()
@@ -103,6 +132,7 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "kind": "oracle",
         "sample": f"{w.name}: head 0, step 0, query frames 0..{done - 1} ({done} of {w.T} frames × {w.H} heads), "
                   f"float64 torch-CPU, {dt:.1f} s, {threads} threads of {os.cpu_count()} host CPUs",
+        "oracle_mask_us_per_step": round(mask_us, 1),
     }
 
 
@@ -328,6 +358,8 @@ def main():
                     help="run a plain 1 GiB device-to-device copy first (reference for HBM byte counters)")
     ap.add_argument("--sweep", action="store_true", help="time every workload (table on stderr)")
     ap.add_argument("--sweep-out", default=None, help="also write the sweep table (markdown) here")
+    ap.add_argument("--library", default=None, help="time this build of liblvsa.so instead of the package's (A/B)")
+    ap.add_argument("--no-peak-probe", action="store_true", help="skip the matrix-core peak microbenchmark")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -335,8 +367,11 @@ def main():
         sys.exit(2)
 
     import torch
+    import block_sparse_attention_lvsa_amd as L
     from block_sparse_attention_lvsa_amd.synth import WORKLOADS
 
+    if args.library:
+        L.LIB_PATH = os.path.abspath(args.library)
     if args.sweep:
         lines = ["| workload | B·H, T×P, C/W | ms/call (median) | effective TFLOP/s | % of 2.5 PF | dense (C=T) ms | "
                  "speedup | ideal T/C | torch SDPA flash, dense ms (outside reference) | "
@@ -389,12 +424,36 @@ def main():
                 f"{r['speedup_vs_torch_sdpa_flash_dense']:.2f}x faster")
 
     achieved = r["kernel_tflops"]
+    k_ms = r["kernel_ms"]["avg"]
+    alg_bytes = 8.0 * w.B * w.H * w.N * w.D  # Q, K, V read once, O written once (bf16)
+    span = w.P >= 384
+    kname = "lvsa_attn_fwd<%d,%d,%s>" % ((w.D, 12, "span") if span else (w.D, 4, "frame"))
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(w),
-            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
-            "kernel": "lvsa_attn_fwd<128,4>" + (" (+ lvsa_key_norms<128> and lvsa_combine<128,4> in the timed call)"
-                                                if not args.no_workspace else ""),
-            "kernel_ms_avg": round(r["kernel_ms"]["avg"], 4)}
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "kernel": kname + (" (+ lvsa_key_norms and lvsa_combine, in the timed call)" if not args.no_workspace
+                               else ""),
+            "kernel_ms_avg": round(k_ms, 4),
+            "achieved_is": "algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d per call / HIP-event time of the whole call"}
+    if not args.no_peak_probe:
+        ptf, pmhz = mfma_peak_probe()
+        if ptf:
+            log(f"measured bf16 MFMA peak: {ptf:.0f} TFLOP/s at {pmhz:.0f} MHz (vendor {PEAK_BF16_TFLOPS:.0f})")
+            roof["peak_measured"] = {"value": round(ptf, 1), "unit": "TFLOP/s", "clock_mhz": round(pmhz),
+                                     "what": "libmfma_peak.so: independent v_mfma_f32_32x32x16_bf16 chains on "
+                                             "every SIMD at 3 waves/SIMD, no memory traffic, after a warm-up"}
+            roof["frac_of_measured_peak"] = round(achieved / ptf, 4)
+    tr = measured_traffic(w)
+    if tr:
+        b = tr["bytes_per_launch"]
+        roof["traffic"] = b
+        roof["traffic_what"] = ("L2-to-fabric bytes per launch of the attention kernel (rocprofv3 FETCH_SIZE + "
+                                "WRITE_SIZE, scaled by a plain 1 GiB copy): what left the L2s for the memory "
+                                "side, served by the MALL or by HBM (no counter here tells the two apart)")
+        roof["traffic_spread"] = tr.get("spread")
+        roof["traffic_over_algorithmic"] = round(b / alg_bytes, 2)
+        roof["traffic_gbs"] = round(b / (k_ms * 1e-3) / 1e9, 1)
+        roof["traffic_frac_of_hbm_peak"] = round(b / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        roof["traffic_profile"] = tr.get("profile")
 
     cpu = None
     if not args.no_cpu_baseline:

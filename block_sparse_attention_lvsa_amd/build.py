@@ -3,7 +3,9 @@
     python -m block_sparse_attention_lvsa_amd.build
 
 Compiles every source on each call (hipcc cross-compiles gfx950 without a
-GPU).  Output: ``block_sparse_attention_lvsa_amd/liblvsa.so``.
+GPU).  Output: ``block_sparse_attention_lvsa_amd/liblvsa.so``, and
+``libmfma_peak.so``, the benchmark's matrix-core peak probe (not part of
+the attention library).
 """
 
 from __future__ import annotations
@@ -20,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblvsa.so")
+PEAK_LIB = os.path.join(PKG, "libmfma_peak.so")
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -71,6 +74,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    _run([hipcc, "-x", "hip", f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-shared",
+          os.path.join(CSRC, "mfma_peak.hip"), "-o", tmp])
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 
