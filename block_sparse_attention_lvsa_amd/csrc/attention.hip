@@ -8,20 +8,22 @@
 // per-query cost O(C·P·d) -- the sparsity block is a whole frame of P
 // tokens).
 //
-// Work decomposition.  One workgroup = one tile of BM = 32·NW query tokens
-// of one frame t of one (b, h); each of its NW wavefronts owns 32 query
-// rows.  The last tile of a frame is partial when BM does not divide P (Wan
-// latents: P = 1560 = 12·128 + 24); its idle waves only join the loads and
-// barriers, and the SIMDs they sit on run the other resident workgroups'
-// waves meanwhile (packing the remainders of several frames into one tile
-// measured slower: the merged iteration costs more than the idle waves).
+// Work decomposition.  Each wavefront owns 32 query rows.  Frames of at
+// least 384 tokens (every video workload): a workgroup is 12 wavefronts, the
+// 384 consecutive query tokens [384·i, 384·i + 384) of one (b, h), one
+// workgroup per CU (3 waves per SIMD), so every K/V tile brought into LDS
+// serves 384 rows.  Such an item may cross one frame boundary: it then
+// walks the union of the two frames' key lists, and each wave computes only
+// the key frames its rows attend -- a wave whose rows straddle the boundary
+// masks, per lane, the frames only one of its two frames attends.  Shorter
+// frames: a workgroup is 4 wavefronts, 128 rows of one frame (3 per CU).
 //
-// Key iteration.  The workgroup walks its CSR row once, merging consecutive
-// key frames into runs: tokens are frame-major, so a run of frames [f0, f1]
-// is the one contiguous token range [f0·P, (f1+1)·P).  Each run is streamed
-// in tiles of BN keys; only the last tile of a run is partial, and its
-// missing keys are masked.
-//
+// Key iteration.  The walk merges consecutive key frames with the same
+// membership into segments: tokens are frame-major, so frames [f0, f1] are
+// the one contiguous token range [f0·P, (f1+1)·P).  Each segment is
+// streamed in tiles of BN keys; only the last tile of a segment is partial,
+// and its missing keys are masked.
+
 // Per key tile, per wave (all on the matrix cores, bf16 -> fp32):
 //   Sᵀ(32 keys × 32 queries) = K · Qᵀ    v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                         Q held in VGPRs for the whole loop.
@@ -45,9 +47,9 @@
 // every MFMA operand read is bank-conflict free.
 //
 // Launch order.  Workgroups are dispatched round-robin over the 8 XCDs; each
-// XCD receives a contiguous range of (b, h, t, query-tile) work items: the
-// query tiles of a frame and neighbouring frames (which share most of their
-// key frames) run on the same XCD and hit in its L2.  With a workspace the
+// XCD receives a contiguous range of work items (in token order): the query
+// tiles of a frame and neighbouring frames (which share most of their key
+// frames) run on the same XCD and hit in its L2.  With a workspace the
 // items are taken from per-XCD counters, so XCDs that clock faster take over
 // work from slower ones (see the work-item block in the kernel).
 #include <hip/hip_runtime.h>

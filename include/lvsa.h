@@ -80,17 +80,21 @@ typedef struct lvsa_tensor {
   int32_t dtype; /* LVSA_DTYPE_BF16 */
 } lvsa_tensor;
 
-/* ABI version (LVSA_ABI_VERSION). */
+/* ABI version (LVSA_ABI_VERSION).  A library convention; no passage of the
+ * pages defines it. */
 int lvsa_version(void);
 
 /* Message describing the last failure on this thread ("" if none).  The
  * string is owned by the library and valid until the next call on this
- * thread. */
+ * thread.  A library convention; no passage of the pages defines it. */
 const char *lvsa_last_error(void);
 
 /* Number of col_idx entries lvsa_build_mask writes for (T, C, W):
- * T * min(C, T).  Same argument domain as lvsa_build_mask (step and flags
- * do not change the size).  Errors: LVSA_ERR_ARG. */
+ * T * min(C, T), every query frame keeping exactly the budget of key frames
+ * (TechWalker article, §二: the window is extended until the effective
+ * count is back at the target C; fewer than C frames exist when T < C).
+ * Same argument domain as lvsa_build_mask (step and flags do not change
+ * the size).  Errors: LVSA_ERR_ARG. */
 int lvsa_mask_nnz(int32_t T, int32_t C, int32_t W, int32_t *nnz_out);
 
 /* Host mask builder: the key frames of every query frame at one denoising
@@ -148,7 +152,8 @@ int lvsa_build_mask_steps(int32_t T, int32_t C, int32_t W, int32_t step0, int32_
                           int32_t flags, int32_t *row_ptr, int32_t *col_idx, int64_t cap,
                           lvsa_mask_info *info);
 
-/* Host check of a CSR frame mask (any source): row_ptr[0] == 0,
+/* Host check of a CSR frame mask (any source), a library convention (the
+ * pages define no mask format): row_ptr[0] == 0,
  * non-decreasing, row_ptr[T] == nnz, every row non-empty, ascending, unique
  * and within [0, T).  Errors: LVSA_ERR_ARG (null/negative sizes),
  * LVSA_ERR_MASK (the first violation, described by lvsa_last_error()). */
@@ -196,15 +201,27 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
                    void *stream);
 
 /* Bytes of device workspace lvsa_attention_ws needs for tensors of B, H, N
- * tokens and head size D split into T frames: one float per (b, h, frame)
- * rounded up to 256, 256 bytes of work counters, and room for the partial
- * results of the items that run as two halves (about 107 MB at D = 128
- * once there are at least 3,072 query tiles; none below 32).
+ * tokens and head size D split into T frames (a library convention; the
+ * pages define no workspace): one float per (b, h, frame) rounded up to
+ * 256, 256 bytes of work counters, and room for the partial results of the
+ * work items that run as two halves (see lvsa_attention_ws: at most 32 per
+ * XCD of 12-wave records when frames hold >= 384 tokens, 96 of 4-wave
+ * records otherwise; about 107 MB at D = 128 once there are enough items,
+ * none below 32 items).
  * Errors: LVSA_ERR_ARG, LVSA_ERR_SHAPE (D not 64/128, N % T != 0). */
 int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t T, int64_t *bytes);
 
-/* lvsa_attention with a caller-provided device workspace, used to drop the
- * online softmax's running maximum where that is safe.
+/* Work items (both attention entry points).  Frames of at least 384 tokens
+ * (every video workload): items of 384 consecutive query tokens of one
+ * (b, h), run by 12-wave workgroups, one per CU; an item that crosses a
+ * frame boundary walks the union of the two frames' rows, each wave (or,
+ * for a wave whose 32 rows straddle the boundary, each row) taking only its
+ * own frame's key frames.  Shorter frames: items of 128 rows of one frame,
+ * 4-wave workgroups.  Items are cut into 8 contiguous ranges, one per XCD.
+ *
+ * lvsa_attention with a caller-provided device workspace (a library
+ * convention: the pages define the computation, not this split of it),
+ * used to drop the online softmax's running maximum where that is safe.
  *
  * Source: the same computation as lvsa_attention (gist.science explainer,
  * Technical Summary §2).  The workspace changes only the softmax's reference
@@ -215,9 +232,12 @@ int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, i
  * 2·R_i <= 96 (every row's largest probability then >= 2^-96) takes R_i as
  * a fixed reference -- no running maximum, no rescaling, and the subtraction
  * folded into the Q·K^T product (its Q rows are pre-scaled by
- * scale·log2(e) and rounded to bf16).  Other waves keep the running-maximum
- * path of lvsa_attention, bit for bit.  Results agree with lvsa_attention
- * to the same accuracy, not bit for bit.
+ * scale·log2(e) and rounded to bf16, one extra rounding: relative RMS error
+ * about 2.9e-3 against 2.3e-3 for lvsa_attention on unit-variance inputs).
+ * Other waves keep the running-maximum arithmetic of lvsa_attention.
+ * Results agree with lvsa_attention to that accuracy, not bit for bit; rows
+ * whose waves all fall back are bit-identical unless their work item runs
+ * as two merged halves (below), which rounds differently.
  *
  * The workspace also holds one work counter per XCD: workgroups take their
  * (b, h, frame, query tile) items from counters instead of a fixed split,
