@@ -340,8 +340,15 @@ def test_workspace_mid_size(gpu, case):
         o = L.lvsa_attention(qd, kd, vd, m, workspace=ws)
         o_exact = L.lvsa_attention(qd, kd, vd, m)
         torch.cuda.synchronize()
-        assert_close(o, oa.block_attention(q, k, v, om.key_frames(T, C, W, s)), f"ws mid {case} step {s}")
+        ref = oa.block_attention(q, k, v, om.key_frames(T, C, W, s))
+        assert_close(o, ref, f"ws mid {case} step {s}")
         assert_close(o, o_exact.double().cpu(), f"ws vs exact path, step {s}")
+        # The fixed reference pre-scales Q by scale*log2(e) and rounds it to
+        # bf16 once more: a bounded accuracy cost against the running-max
+        # path (measured relRMS ratio 1.2-1.25 on unit-variance inputs).
+        rel_ws, rel_rm = stats(o, ref)[2], stats(o_exact, ref)[2]
+        print(f"  relRMS workspace {rel_ws:.3e} vs running max {rel_rm:.3e}", flush=True)
+        assert rel_ws <= 1.5 * rel_rm + 1e-4, (rel_ws, rel_rm)
 
 
 def test_workspace_takes_a_fixed_reference_and_falls_back_on_large_norms(gpu):
