@@ -291,7 +291,11 @@ template <int D, int NW>
 struct Block {
   using C = Cfg<D, NW>;
 
-  char *lds;
+  // LDS tile buffers 0 and 1, {K, V} each.  Two arrays rather than one, so
+  // the compiler sees that the direct-to-LDS loads into one buffer cannot
+  // touch the other and does not wait for them before the tile's V reads.
+  char *lds0, *lds1;
+  __device__ __forceinline__ char *bufp(int buf) const { return buf ? lds1 : lds0; }
   int lane, wave, l32, hf;
   float scale_log2;
   bf16x8_t qf[D / 16];         // the wave's Q rows, B-operand layout
@@ -303,8 +307,8 @@ struct Block {
   int32_t vro[D / 32];         // LDS byte offsets of this lane's V source rows
   int32_t koffb[C::LOADS_PER_WAVE], voffb[C::LOADS_PER_WAVE];  // load byte offsets
 
-  static constexpr int kTileOffK(int buf) { return buf * 2 * C::TILE_BYTES; }
-  static constexpr int kTileOffV(int buf) { return buf * 2 * C::TILE_BYTES + C::TILE_BYTES; }
+  static constexpr int kTileOffK = 0;             // within a buffer
+  static constexpr int kTileOffV = C::TILE_BYTES;
 
   __device__ __forceinline__ void init_offsets(int32_t k_sn, int32_t v_sn) {
     // Load i of loading wave lw covers keys key0 + i·KEYS_PER_LOAD (one per
@@ -346,7 +350,7 @@ struct Block {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, nrec, kBufferFlags);
     const int lw = wave - C::FIRST_LOADER;
     if (lw < 0) return;  // wave-uniform
-    char *dst = lds + (IS_V ? kTileOffV(buf) : kTileOffK(buf)) + lw * C::LOADS_PER_WAVE * 1024;
+    char *dst = bufp(buf) + (IS_V ? kTileOffV : kTileOffK) + lw * C::LOADS_PER_WAVE * 1024;
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
@@ -358,7 +362,7 @@ struct Block {
   // (the wave's Q rows are then pre-scaled by scale·log2e).
   template <int KBUF, bool FIXED>
   __device__ __forceinline__ void qk(f32x16_t (&sc)[C::KB]) const {
-    const char *Kb = lds + kTileOffK(KBUF);
+    const char *Kb = bufp(KBUF) + kTileOffK;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) sc[kb] = FIXED ? bias : f32x16_t{};
 #pragma unroll
@@ -451,7 +455,7 @@ struct Block {
   // Oᵀ += Vᵀ·Pᵀ with the V tile in buffer VBUF.
   template <int VBUF>
   __device__ __forceinline__ void pv(const bf16x8_t (&pb)[2 * C::KB]) {
-    const char *Vb = lds + kTileOffV(VBUF);
+    const char *Vb = bufp(VBUF) + kTileOffV;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -539,10 +543,12 @@ template <int D, int NW, bool SPAN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
 void lvsa_attn_fwd(Args a) {
   using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];  // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(1024))) char lds0[C::LDS_BYTES / 2];  // K0 V0
+  __shared__ __attribute__((aligned(1024))) char lds1[C::LDS_BYTES / 2];  // K1 V1
 
   Block<D, NW> blk;
-  blk.lds = lds;
+  blk.lds0 = lds0;
+  blk.lds1 = lds1;
   const int tid = threadIdx.x;
   blk.lane = tid & 63;
   blk.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -568,7 +574,7 @@ void lvsa_attn_fwd(Args a) {
     // the barrier that precedes the loads into buffer 1.  (A separate
     // __shared__ word measured 2.5-6% slower, from the code it changes: more
     // LDS alone, up to 48 KB per workgroup, costs nothing.)
-    int *const s_item = reinterpret_cast<int *>(lds + 2 * C::TILE_BYTES);
+    int *const s_item = reinterpret_cast<int *>(lds1);
     if (tid == 0) {
       unsigned xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
