@@ -433,10 +433,10 @@ def main():
     k_ms = r["kernel_ms"]["avg"]
     alg_bytes = 8.0 * w.B * w.H * w.N * w.D  # Q, K, V read once, O written once (bf16)
     span = w.P >= 384
-    kname = "lvsa_attn_fwd<%d,%d,%s>" % ((w.D, 12, "span") if span else (w.D, 4, "frame"))
+    kname = ("lvsa_attn_span<%d>" if span else "lvsa_attn_frame<%d>") % w.D
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-            "kernel": kname + (" (+ lvsa_key_norms and lvsa_combine, in the timed call)" if not args.no_workspace
+            "kernel": kname + (" (+ lvsa_key_norms and the merge of split items, in the timed call)" if not args.no_workspace
                                else ""),
             "kernel_ms_avg": round(k_ms, 4),
             "achieved_is": "algorithmic FLOPs 4·B·H·T·min(C,T)·P²·d per call / HIP-event time of the whole call"}

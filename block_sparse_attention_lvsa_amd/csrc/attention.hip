@@ -8,37 +8,39 @@
 // per-query cost O(C·P·d) -- the sparsity block is a whole frame of P
 // tokens).
 //
-// Work decomposition.  Each wavefront owns 32 query rows.  Frames of at
-// least 384 tokens (every video workload): a workgroup is 12 wavefronts, the
-// 384 consecutive query tokens [384·i, 384·i + 384) of one (b, h), one
-// workgroup per CU (3 waves per SIMD), so every K/V tile brought into LDS
-// serves 384 rows.  Such an item may cross one frame boundary: it then
-// walks the union of the two frames' key lists, and each wave computes only
-// the key frames its rows attend -- a wave whose rows straddle the boundary
-// masks, per lane, the frames only one of its two frames attends.  Shorter
-// frames: a workgroup is 4 wavefronts, 128 rows of one frame (3 per CU).
+// Two kernels, one per kind of work item (bf16 MFMA, fp32 accumulation):
+//
+//   lvsa_attn_span (frames of at least 384 tokens: every video workload).
+//   A work item is the 384 consecutive query tokens [384·i, 384·i + 384) of
+//   one (b, h); a workgroup is 8 waves of 48 rows, one per CU (2 waves per
+//   SIMD), so every K/V tile brought into LDS serves 384 rows.  Each wave
+//   computes its rows as three 16-row blocks with v_mfma_f32_16x16x32_bf16:
+//   every K and Vᵀ operand read from LDS feeds the MFMAs of all three blocks.
+//   An item may cross one frame boundary: it then walks the union of the two
+//   frames' key lists, and each wave computes only the key frames its rows
+//   attend -- a wave whose rows straddle the boundary masks, per row, the
+//   frames only one of its two frames attends.
+//
+//   lvsa_attn_frame (shorter frames).  A work item is 128 rows of one frame;
+//   a workgroup is 4 waves of 32 rows (3 workgroups per CU), with
+//   v_mfma_f32_32x32x16_bf16.
 //
 // Key iteration.  The walk merges consecutive key frames with the same
 // membership into segments: tokens are frame-major, so frames [f0, f1] are
 // the one contiguous token range [f0·P, (f1+1)·P).  Each segment is
-// streamed in tiles of BN keys; only the last tile of a segment is partial,
+// streamed in tiles of 32 keys; only the last tile of a segment is partial,
 // and its missing keys are masked.
-
-// Per key tile, per wave (all on the matrix cores, bf16 -> fp32):
-//   Sᵀ(32 keys × 32 queries) = K · Qᵀ    v_mfma_f32_32x32x16_bf16, K from LDS,
-//                                         Q held in VGPRs for the whole loop.
-//   In the 32x32 accumulator layout lane l holds query l%32 and keys
-//   8i + 4(l/32) + j, so a query's row lives in lanes l and l^32: the row
-//   max and sum are per-lane reductions plus one permlane32 swap.
-//   Online softmax in the log2 domain with a lazily updated running max
-//   (rescale only when the tile max exceeds it by more than 2^8, so exp2
-//   arguments stay <= 8 and fp32 cannot overflow); or, given per-frame
-//   key norms, a fixed per-row reference from a Cauchy-Schwarz bound,
-//   subtracted by starting the Q·Kᵀ chain from it.
-//   Oᵀ(d × 32 queries) += Vᵀ · Pᵀ         P (bf16) comes straight from the Sᵀ
-//                                         accumulator registers; the Vᵀ
-//                                         operand is built by transposing
-//                                         LDS reads (ds_read_b64_tr_b16).
+//
+// Per key tile, per wave (all on the matrix cores):
+//   Sᵀ = K · Qᵀ     K from LDS, Q held in VGPRs for the whole walk.
+//   Softmax in the log2 domain, per query row: with a lazily updated running
+//   max (rescale only when the tile max exceeds it by more than 2^8, so exp2
+//   arguments stay <= 8 and fp32 cannot overflow); or, given per-frame key
+//   norms, a fixed reference from a Cauchy-Schwarz bound, subtracted by
+//   starting the Q·Kᵀ chains from it.
+//   Oᵀ += Vᵀ · P    P (bf16) comes straight from the Sᵀ accumulator
+//                   registers; the Vᵀ operand is built by transposing LDS
+//                   reads (ds_read_b64_tr_b16).
 //
 // K/V staging.  Each tile's K and V rows go from global memory straight into
 // LDS (buffer loads with the LDS-destination bit, 16 bytes per lane), double
@@ -51,7 +53,7 @@
 // tiles of a frame and neighbouring frames (which share most of their key
 // frames) run on the same XCD and hit in its L2.  With a workspace the
 // items are taken from per-XCD counters, so XCDs that clock faster take over
-// work from slower ones (see the work-item block in the kernel).
+// work from slower ones (take_item).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -84,9 +86,9 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint16_t u16;
 
-// Tuning knobs (compile-time): the register budget expressed as resident
-// waves per SIMD, keys per tile, and how many K operand reads run ahead of
-// the Q·Kᵀ MFMA chain.
+// Tuning knobs of the frame kernel (compile-time): the register budget
+// expressed as resident waves per SIMD, keys per tile, and how many K
+// operand reads run ahead of the Q·Kᵀ MFMA chain.
 #ifndef LVSA_WAVES_PER_SIMD
 #define LVSA_WAVES_PER_SIMD 3
 #endif
@@ -98,6 +100,8 @@ typedef uint16_t u16;
 #endif
 
 constexpr int kNumXcd = 8;          // XCDs per MI355X
+constexpr int kFrameWaves = 4;      // waves per workgroup of the frame kernel
+constexpr int kSpanRows = 384;      // query rows per work item of the span kernel
 constexpr float kMaxLag = 8.0f;     // log2 slack of the lazily updated row max
 // Largest log2 gap a fixed softmax reference may leave below a row's true
 // maximum: with the reference at most 96 above it (its bound, below), the
@@ -120,9 +124,10 @@ struct Args {
   // workgroup i runs the (i mod 8)-th XCD's (i div 8)-th item.
   int *tickets;
   // With tickets: the last min(split_cap, range / 4) items of each XCD
-  // range run as two halves of their CSR row, whose partial results (records
-  // of kPartialFloats(D) floats per lane, slot x·split_cap + j) go to
-  // `partial` and are merged by lvsa_combine; split_cap = 0 splits nothing.
+  // range run as two halves of their key walk, whose partial results
+  // (records of kPartialFloats(D) or kSpanPartialFloats(D) floats per lane,
+  // slot x·split_cap + j) go to `partial` and are merged by the combine
+  // kernel; split_cap = 0 splits nothing.
   float *partial;
   int32_t split_cap;
 };
@@ -471,27 +476,13 @@ struct Block {
       }
   }
 
-  // Removes the whole tile from the rows of the lanes not set in `keep`
-  // (a wave whose rows cross a frame boundary, on key frames only one of
-  // the two frames attends).
-  __device__ __forceinline__ void mask_lanes(f32x16_t (&sc)[C::KB], uint64_t keep) {
-    asm volatile("" ::: "memory");  // keep the wave-uniform branch around it a branch
-    const bool ok = (keep >> lane) & 1;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[kb][e] = ok ? sc[kb][e] : -INFINITY;
-  }
-
-  // One key tile from LDS buffer BUF.  lane_mask: whether only the lanes in
-  // `keep` attend it.
+  // One key tile from LDS buffer BUF.
   template <int BUF, bool FIXED>
-  __device__ __forceinline__ void tile(int kv, bool lane_mask, uint64_t keep) {
+  __device__ __forceinline__ void tile(int kv) {
     f32x16_t sc[C::KB];
     bf16x8_t pb[2 * C::KB];
     qk<BUF, FIXED>(sc);
     mask_tail(sc, kv);
-    if (lane_mask) mask_lanes(sc, keep);
     if constexpr (!FIXED) fold_max(sc);
     probs<FIXED>(sc, pb);
     pv<BUF>(pb);
@@ -529,53 +520,26 @@ __device__ __forceinline__ Item decode_item(const Args &a, int item) {
   return it;
 }
 
-// The entries [rb, re) of CSR row t, offsets clamped to [0, nnz].
-__device__ __forceinline__ void row_range(const Args &a, int t, int32_t *rb, int32_t *re) {
-  const const_i32p rp = (const_i32p)a.row_ptr;
-  int32_t b = rp[t], e = rp[t + 1];
-  b = b < 0 ? 0 : (b > a.nnz ? a.nnz : b);
-  e = e < b ? b : (e > a.nnz ? a.nnz : e);
-  *rb = b;
-  *re = e;
-}
-
-template <int D, int NW, bool SPAN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD)))
-void lvsa_attn_fwd(Args a) {
-  using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char lds0[C::LDS_BYTES / 2];  // K0 V0
-  __shared__ __attribute__((aligned(1024))) char lds1[C::LDS_BYTES / 2];  // K1 V1
-
-  Block<D, NW> blk;
-  blk.lds0 = lds0;
-  blk.lds1 = lds1;
-  const int tid = threadIdx.x;
-  blk.lane = tid & 63;
-  blk.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  blk.l32 = blk.lane & 31;
-  blk.hf = blk.lane >> 5;
-  blk.scale_log2 = a.scale_log2;
-
-  // ---- work item.  The items are split into 8 contiguous ranges, one per
-  // XCD, so that the query tiles of a frame and neighbouring frames (which
-  // share most key frames) run on one XCD and share its L2.  Statically,
-  // workgroup i runs the (i div 8)-th item of XCD i mod 8's range (the
-  // dispatcher deals workgroups round-robin over the XCDs).  With ticket
-  // counters, a workgroup takes the next item of the range of the XCD it
-  // runs on, and once that range is used up, of the others: the XCDs of one
-  // part run at different speeds (up to ~7% apart), and a static split
-  // leaves the fast ones idle while the slowest finishes.  More workgroups
-  // than items are launched; the ones that find no item left exit.
-  int item, half = -1, slot = 0;
+// ---- work items.  The items are split into 8 contiguous ranges, one per
+// XCD, so that the query tiles of a frame and neighbouring frames (which
+// share most key frames) run on one XCD and share its L2.  Statically,
+// workgroup i runs the (i div 8)-th item of XCD i mod 8's range (the
+// dispatcher deals workgroups round-robin over the XCDs).  With ticket
+// counters, a workgroup takes the next item of the range of the XCD it runs
+// on, and once that range is used up, of the others: the XCDs of one part
+// run at different speeds (up to ~7% apart), and a static split leaves the
+// fast ones idle while the slowest finishes.  More workgroups than items are
+// launched; the ones that find no item left exit (returns false: uniform,
+// all waves leave).
+//
+// The item (and, for a half, which half and its record slot) is broadcast
+// through s_item, the first words of LDS tile buffer 1: the first tile loads
+// (buffer 0) do not touch them, and every wave reads them before the barrier
+// that precedes the loads into buffer 1.  (A separate __shared__ word
+// measured 2.5-6% slower, from the code it changes.)
+__device__ __forceinline__ bool take_item(const Args &a, int *s_item, int *item, int *half, int *slot) {
   if (a.tickets) {
-    // The item (and, for a half, which half and its record slot) is
-    // broadcast through the first words of LDS tile buffer 1: the first tile
-    // loads (buffer 0) do not touch them, and every wave reads them before
-    // the barrier that precedes the loads into buffer 1.  (A separate
-    // __shared__ word measured 2.5-6% slower, from the code it changes: more
-    // LDS alone, up to 48 KB per workgroup, costs nothing.)
-    int *const s_item = reinterpret_cast<int *>(lds1);
-    if (tid == 0) {
+    if (threadIdx.x == 0) {
       unsigned xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
       int got = -1, gh = -1, gs = 0;
@@ -603,18 +567,109 @@ void lvsa_attn_fwd(Args a) {
       s_item[2] = gs;
     }
     __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(s_item[0]);
-    half = __builtin_amdgcn_readfirstlane(s_item[1]);
-    slot = __builtin_amdgcn_readfirstlane(s_item[2]);
-    if (item < 0) return;  // every item is taken (uniform: all waves leave)
-  } else {
-    const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
-    int base, cnt;
-    xcd_range(a.n_wg, x, &base, &cnt);
-    item = base + j;
+    *item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    *half = __builtin_amdgcn_readfirstlane(s_item[1]);
+    *slot = __builtin_amdgcn_readfirstlane(s_item[2]);
+    return *item >= 0;
   }
-  const Item wi = decode_item<C::BM, SPAN>(a, item);
-  const int P = a.P;
+  const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+  int base, cnt;
+  xcd_range(a.n_wg, x, &base, &cnt);
+  *item = base + j;
+  *half = -1;
+  *slot = 0;
+  return true;
+}
+
+// The entries [rb, re) of CSR row t, offsets clamped to [0, nnz].
+__device__ __forceinline__ void row_range(const Args &a, int t, int32_t *rb, int32_t *re) {
+  const const_i32p rp = (const_i32p)a.row_ptr;
+  int32_t b = rp[t], e = rp[t + 1];
+  b = b < 0 ? 0 : (b > a.nnz ? a.nnz : b);
+  e = e < b ? b : (e > a.nnz ? a.nnz : e);
+  *rb = b;
+  *re = e;
+}
+
+// The key walk of work item wi: the union of the CSR rows of its frames t0
+// and t1 (one row when t1 = t0), split at frame fm for the two halves of a
+// split item: the first half walks the frames below fm, the second the rest,
+// so that together they walk exactly what the whole walk does.  fm is the
+// middle entry of t0's row (any frame partitions the walk; the middle one
+// halves it for well-formed rows).
+__device__ __forceinline__ SegIter make_walk(const Args &a, const Item &wi, int half) {
+  const bool two = wi.t1 != wi.t0;
+  SegIter it;
+  it.cols = (const_i32p)a.col_idx;
+  it.T = a.T;
+  it.P = a.P;
+  it.f_hi = a.T;
+  row_range(a, wi.t0, &it.e0, &it.end0);
+  if (two)
+    row_range(a, wi.t1, &it.e1, &it.end1);
+  else
+    it.e1 = it.end1 = 0;
+  it.last0 = it.last1 = -1;
+  it.bits0 = two ? 1 : 3;
+  it.ks = it.ke = it.mem = 0;
+  if (half >= 0) {
+    const int32_t mid = it.e0 + (it.end0 - it.e0) / 2;
+    int32_t fm = it.end0 > it.e0 ? it.cols[mid] : 0;
+    fm = fm < 0 ? 0 : (fm > a.T ? a.T : fm);
+    if (half == 0)
+      it.f_hi = fm;
+    else
+      it.skip_below(fm);
+  }
+  return it;
+}
+
+// Tiles of bn keys in a walk.
+__device__ __forceinline__ int walk_tiles(SegIter c, int bn) {
+  int n = 0;
+  while (c.next()) n += (c.ke - c.ks + bn - 1) / bn;
+  return n;
+}
+
+// The largest key norm over the frames of wi's rows, from the per-frame
+// table knorm: every entry of both rows, so that both halves of a split item
+// decide alike.
+__device__ __forceinline__ float walk_key_norm(const Args &a, const Item &wi) {
+  const const_f32p fn = (const_f32p)(a.knorm + (int64_t)wi.bh * a.T);
+  const const_i32p cols = (const_i32p)a.col_idx;
+  float kn = 0.f;
+  for (int r = 0; r < (wi.t1 != wi.t0 ? 2 : 1); ++r) {
+    int32_t rb, re;
+    row_range(a, r ? wi.t1 : wi.t0, &rb, &re);
+    for (int32_t e = rb; e < re; ++e) {
+      const int32_t f = cols[e];
+      if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
+    }
+  }
+  return kn;
+}
+
+template <int D>
+__global__ __launch_bounds__(kFrameWaves * 64)
+__attribute__((amdgpu_waves_per_eu(LVSA_WAVES_PER_SIMD, LVSA_WAVES_PER_SIMD))) void lvsa_attn_frame(Args a) {
+  constexpr int NW = kFrameWaves;
+  using C = Cfg<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char lds0[C::LDS_BYTES / 2];  // K0 V0
+  __shared__ __attribute__((aligned(1024))) char lds1[C::LDS_BYTES / 2];  // K1 V1
+
+  Block<D, NW> blk;
+  blk.lds0 = lds0;
+  blk.lds1 = lds1;
+  const int tid = threadIdx.x;
+  blk.lane = tid & 63;
+  blk.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  blk.l32 = blk.lane & 31;
+  blk.hf = blk.lane >> 5;
+  blk.scale_log2 = a.scale_log2;
+
+  int item, half, slot;
+  if (!take_item(a, reinterpret_cast<int *>(lds1), &item, &half, &slot)) return;
+  const Item wi = decode_item<C::BM, false>(a, item);
   const u16 *kbase = a.k + (int64_t)wi.b * a.k_sb + (int64_t)wi.h * a.k_sh;
   const u16 *vbase = a.v + (int64_t)wi.b * a.v_sb + (int64_t)wi.h * a.v_sh;
 
@@ -634,8 +689,6 @@ void lvsa_attn_fwd(Args a) {
   }
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) blk.oacc[i] = f32x16_t{};
-  // A finite start: a lane whose first tiles are all masked out (see
-  // mask_lanes) then gets probabilities 2^-inf = 0 rather than NaN.
   blk.m_run = -FLT_MAX;
   blk.l_run = 0.f;
   blk.init_offsets(a.k_sn, a.v_sn);
@@ -643,53 +696,10 @@ void lvsa_attn_fwd(Args a) {
   // the sequence may not fill every wave), as a scalar, so the per-tile test
   // is a scalar branch rather than a vector compare.
   const int compute = __builtin_amdgcn_readfirstlane(row0 < wi.tok_end ? 1 : 0);
-  // Which of the walk's frame memberships the wave's rows need (bit 0: rows
-  // in t0, bit 1: rows in t1), and, for a wave whose rows cross the frame
-  // boundary, the lanes whose rows lie in t1.
-  const bool two = wi.t1 != wi.t0;
-  int need = 3;
-  uint64_t lanes_t1 = 0;
-  if (SPAN && two && compute) {
-    const int f_first = row0 / P;
-    const int f_last = min(row0 + 31, wi.tok_end - 1) / P;
-    need = f_first == f_last ? (f_first == wi.t0 ? 1 : 2) : 3;
-    lanes_t1 = __builtin_amdgcn_ballot_w64(my_row / P == wi.t1);
-  }
-  need = __builtin_amdgcn_readfirstlane(need);
 
-  // ---- the key walk: the union of the rows of t0 and t1, split at frame fm
-  // for the two halves of a split item (the first half walks the frames
-  // below fm, the second the rest, so that together they walk exactly what
-  // the whole walk does)
-  SegIter it;
-  it.cols = (const_i32p)a.col_idx;
-  it.T = a.T;
-  it.P = P;
-  it.f_hi = a.T;
-  row_range(a, wi.t0, &it.e0, &it.end0);
-  if (two)
-    row_range(a, wi.t1, &it.e1, &it.end1);
-  else
-    it.e1 = it.end1 = 0;
-  it.last0 = it.last1 = -1;
-  it.bits0 = two ? 1 : 3;
-  it.ks = it.ke = it.mem = 0;
-  if (half >= 0) {
-    // fm: the middle entry of t0's row (any frame partitions the walk; the
-    // middle one halves it for well-formed rows)
-    const int32_t mid = it.e0 + (it.end0 - it.e0) / 2;
-    int32_t fm = it.end0 > it.e0 ? it.cols[mid] : 0;
-    fm = fm < 0 ? 0 : (fm > a.T ? a.T : fm);
-    if (half == 0)
-      it.f_hi = fm;
-    else
-      it.skip_below(fm);
-  }
-  int n_walk = 0;  // tiles this workgroup walks
-  {
-    SegIter c = it;
-    while (c.next()) n_walk += (c.ke - c.ks + C::BN - 1) / C::BN;
-  }
+  // ---- the key walk: the CSR row of the item's frame
+  SegIter it = make_walk(a, wi, half);
+  const int n_walk = walk_tiles(it, C::BN);  // tiles this workgroup walks
 
   // ---- softmax reference.  Without a key-norm table: the running max,
   // raised lazily.  With one: by Cauchy-Schwarz every score of query i lies
@@ -702,18 +712,7 @@ void lvsa_attn_fwd(Args a) {
   // Q·Kᵀ chain's initial accumulator.  Other waves keep the running max.
   bool fixed = false;
   if (a.knorm) {
-    const const_f32p fn = (const_f32p)(a.knorm + (int64_t)wi.bh * a.T);
-    float kn = 0.f;
-    // over the whole walk (both rows, every entry), so that both halves of
-    // a split item decide alike
-    for (int r = 0; r < (two ? 2 : 1); ++r) {
-      int32_t rb, re;
-      row_range(a, r ? wi.t1 : wi.t0, &rb, &re);
-      for (int32_t e = rb; e < re; ++e) {
-        const int32_t f = it.cols[e];
-        if (f >= 0 && f < a.T) kn = fmaxf(kn, fn[f]);
-      }
-    }
+    const float kn = walk_key_norm(a, wi);
     float ss = 0.f;  // |q'_i|^2 of the scaled, rounded rows
 #pragma unroll
     for (int dc = 0; dc < D / 16; ++dc)
@@ -739,9 +738,8 @@ void lvsa_attn_fwd(Args a) {
   // ---- main loop over key tiles: K and V double-buffered in LDS (tile j in
   // buffer j mod 2); the loads of tile j+1 run while tile j is computed; one
   // barrier per tile.  Unrolled by two so that every LDS offset is an
-  // immediate.  A tile is computed by the waves whose rows attend its frame
-  // (every wave, unless the tile's rows cross a frame boundary).
-  int pos = 0, kv = 0, mem = 0;
+  // immediate.
+  int pos = 0, kv = 0;
   auto advance = [&]() {  // next tile, moving to the next segment when needed
     pos += C::BN;
     if (pos >= it.ke) {
@@ -749,7 +747,6 @@ void lvsa_attn_fwd(Args a) {
       pos = it.ks;
     }
     kv = min(C::BN, it.ke - pos);
-    mem = it.mem;
   };
   auto issue = [&](int buf) {
     blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
@@ -759,7 +756,6 @@ void lvsa_attn_fwd(Args a) {
     it.next();
     pos = it.ks;
     kv = min(C::BN, it.ke - pos);
-    mem = it.mem;
     issue(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -768,31 +764,26 @@ void lvsa_attn_fwd(Args a) {
   // workgroup runs the same loads and barriers in either.
   auto run = [&](auto fixed_c) {
     constexpr bool F = decltype(fixed_c)::value;
-    auto step = [&](auto buf_c, int kvj, int memj) {
-      constexpr int BUF = decltype(buf_c)::value;
-      if (compute && (memj & need)) {
-        // a boundary-crossing wave, on a frame only one of its two frames attends
-        const bool lm = need == 3 && memj != 3;
-        blk.template tile<BUF, F>(kvj, lm, memj == 2 ? lanes_t1 : ~lanes_t1);
-      }
+    auto step = [&](auto buf_c, int kvj) {
+      if (compute) blk.template tile<decltype(buf_c)::value, F>(kvj);
     };
     for (int i = 0; i + 1 < n_walk; i += 2) {
-      const int kv0 = kv, mem0 = mem;
+      const int kv0 = kv;
       advance();  // tile i+1 -> buffer 1
       issue(1);
-      step(std::integral_constant<int, 0>{}, kv0, mem0);
+      step(std::integral_constant<int, 0>{}, kv0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      const int kv1 = kv, mem1 = mem;
+      const int kv1 = kv;
       if (i + 2 < n_walk) {  // tile i+2 -> buffer 0
         advance();
         issue(0);
       }
-      step(std::integral_constant<int, 1>{}, kv1, mem1);
+      step(std::integral_constant<int, 1>{}, kv1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if (n_walk & 1) step(std::integral_constant<int, 0>{}, kv, mem);
+    if (n_walk & 1) step(std::integral_constant<int, 0>{}, kv);
   };
   if (fixed)
     run(std::true_type{});
@@ -800,7 +791,7 @@ void lvsa_attn_fwd(Args a) {
     run(std::false_type{});
 
   // ---- a half writes its partial record (unnormalised O, partial row sum,
-  // reference) for lvsa_combine, which runs after this kernel
+  // reference) for lvsa_combine_frame, which runs after this kernel
   if (half >= 0) {
     if (compute) {
       constexpr int R4 = kPartialFloats(D) / 4;
@@ -875,19 +866,20 @@ __global__ __launch_bounds__(256) void lvsa_key_norms(const u16 *k, int64_t k_sb
 }
 
 // Merges the two halves of every split item: one workgroup per record slot,
-// one wave per 32 query rows as in lvsa_attn_fwd.  Each lane reads its two
+// one wave per 32 query rows as in lvsa_attn_frame.  Each lane reads its two
 // partial records (O accumulators, partial row sum l and reference m of its
 // query), rescales both to the larger reference, adds, normalises and
-// stores the item's output rows.  Runs after lvsa_attn_fwd on the same
+// stores the item's output rows.  Runs after lvsa_attn_frame on the same
 // stream, so the records are complete.
-template <int D, int NW, bool SPAN>
-__global__ __launch_bounds__(NW * 64) void lvsa_combine(Args a) {
+template <int D>
+__global__ __launch_bounds__(kFrameWaves * 64) void lvsa_combine_frame(Args a) {
+  constexpr int NW = kFrameWaves;
   const int x = blockIdx.x / a.split_cap, j = blockIdx.x % a.split_cap;
   int base, cnt;
   xcd_range(a.n_wg, x, &base, &cnt);
   const int S = split_count(a.split_cap, cnt);
   if (j >= S) return;
-  const Item wi = decode_item<NW * 32, SPAN>(a, base + (cnt - S) + j);
+  const Item wi = decode_item<NW * 32, false>(a, base + (cnt - S) + j);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = wi.tok0 + wave * 32;
@@ -920,6 +912,529 @@ __global__ __launch_bounds__(NW * 64) void lvsa_combine(Args a) {
       o4[3] = (__bf16)((w0 * o0.w + w1 * o1.w) * inv);
       *reinterpret_cast<bf16x4_t *>(op + dc * 32 + i * 8 + (lane >> 5) * 4) = o4;
     }
+}
+
+// ------------------------------------------------------------ span kernel --
+// Frames of at least kSpanRows tokens (every video workload).  A workgroup
+// is 8 waves, one per CU (2 waves per SIMD), over the kSpanRows consecutive
+// query tokens of a work item; each wave owns 48 rows as three 16-row
+// blocks and uses v_mfma_f32_16x16x32_bf16, so that every K operand read
+// from LDS feeds the Q·Kᵀ MFMAs of all three blocks and every Vᵀ operand
+// read the P·V MFMAs of all three: a third fewer LDS bytes per flop than
+// waves of 32 rows with the 32x32x16 MFMA.
+//
+// Lane layouts of v_mfma_f32_16x16x32_bf16 (64 lanes, l = 16g + s):
+//   A (16 x 32): lane l holds A[s][8g + e], e = 0..7 (8 bf16)
+//   B (32 x 16): lane l holds B[8g + e][s]
+//   C (16 x 16): lane l holds C[4g + r][s], r = 0..3 (4 fp32)
+// Per tile of 32 keys, per wave:
+//   Sᵀ(16 keys × 16 queries), for 2 key blocks × 3 query blocks: A = K rows
+//     (key 16kbk + s, dims 32dc + 8g + e), B = the wave's Q rows (held in
+//     VGPRs), D/32 reduction steps; lane l then holds query 16qb + s and
+//     keys 16kbk + 4g + r, so a query's row lies in lanes s, s+16, s+32,
+//     s+48 (row reductions: two lane swaps).
+//   P (bf16) of query block qb is the B operand of P·V as it stands: k-slot
+//     8g + 4kbk + r is key 16kbk + 4g + r.
+//   Oᵀ(16 dims × 16 queries) += Vᵀ · P for D/16 dim blocks × 3 query blocks;
+//     the Vᵀ operand (dim 16db + s, the same eight keys per lane as P's
+//     k-slots) comes from two transposing LDS reads of four keys each.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kQB = 3;  // 16-row query blocks per wave
+// Floats per lane in a partial record of the span kernel: the lane's Oᵀ
+// accumulators (3 × D/16 × 4), its three partial row sums and references,
+// padding to 16 bytes.
+__host__ __device__ constexpr int kSpanPartialFloats(int d) { return kQB * d / 4 + 8; }
+
+template <int D>
+struct SpanCfg {
+  static constexpr int NW = 8;                  // waves per workgroup (2 per SIMD)
+  static constexpr int BM = NW * 16 * kQB;      // query rows per workgroup
+  static_assert(BM == kSpanRows, "work item size");
+  static constexpr int BN = 32;                 // keys per LDS tile
+  static constexpr int CH = D / 8;              // 16-byte chunks per key row
+  static constexpr int ROWB = D * 2;            // bytes per key row
+  static constexpr int TILE_BYTES = BN * ROWB;
+  static constexpr int LOADS = TILE_BYTES / 1024;  // 1 KB wave loads per tile
+  // The loads are issued by the last four waves, the younger wave of each
+  // SIMD, so that the older one goes straight to its matrix work after a
+  // barrier (the sequencer favours older waves): measured 1-2% faster than
+  // one load of each per wave from all eight.
+  static constexpr int LOADS_PER_WAVE = LOADS >= 4 ? LOADS / 4 : 1;
+  static constexpr int NLOADERS = LOADS / LOADS_PER_WAVE;
+  static constexpr int FIRST_LOADER = NW - NLOADERS;
+  static constexpr int VSW = CH / 4;            // V swizzle step
+  static constexpr int KEYS_PER_LOAD = 64 / CH;
+  static constexpr int DC = D / 32;             // 32-dim reduction steps of Q·Kᵀ
+  static constexpr int DB = D / 16;             // 16-dim blocks of O
+  static constexpr int LDS_BYTES = 2 * 2 * TILE_BYTES;  // {K, V} × 2 buffers
+  static_assert(LOADS % LOADS_PER_WAVE == 0 && NLOADERS <= NW, "tile loads must split evenly over the loading waves");
+};
+
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+// Max and sum over the four lanes s, s+16, s+32, s+48 that hold one query
+// row of a 16x16 accumulator.
+__device__ __forceinline__ float row4_max(float x) { return swap_halves_max(xor16_max(x)); }
+__device__ __forceinline__ float row4_sum(float x) { return swap_halves_sum(xor16_sum(x)); }
+
+// One wave's state and steps in the span kernel (48 query rows).  The LDS
+// tile layout is the frame kernel's: K chunk c of key j at c ^ (j mod CH),
+// V chunk c at c ^ (VSW·(j mod 4)), so both operand reads below are
+// bank-conflict free.
+template <int D>
+struct SpanBlock {
+  using C = SpanCfg<D>;
+  char *lds0, *lds1;  // tile buffers 0 and 1, {K, V} each (separate arrays, as in Block)
+  __device__ __forceinline__ char *bufp(int buf) const { return buf ? lds1 : lds0; }
+  int lane, wave, s16, g;  // lane = 16g + s16
+  float scale_log2;
+  bf16x8_t qf[kQB][C::DC];   // Q rows, B operand: query 16qb + s16, dims 32dc + 8g + e
+  f32x4_t oacc[kQB][C::DB];  // Oᵀ blocks: dims 16db + 4g + r of query 16qb + s16
+  f32x4_t bias[kQB];         // with a fixed reference R: -R, the Q·Kᵀ chains' initial value
+  float m_run[kQB], l_run[kQB];  // per query block: reference (log2 domain), partial row sum
+  int32_t kro[C::DC], vro[C::DB];  // LDS byte offsets of this lane's K and Vᵀ operands
+  int32_t koffb[C::LOADS_PER_WAVE], voffb[C::LOADS_PER_WAVE];  // load byte offsets
+  static constexpr int kTileOffK = 0;  // within a buffer
+  static constexpr int kTileOffV = C::TILE_BYTES;
+
+  __device__ __forceinline__ void init_offsets(int32_t k_sn, int32_t v_sn) {
+    const int lw = max(wave - C::FIRST_LOADER, 0);
+    const int key0 = lw * C::LOADS_PER_WAVE * C::KEYS_PER_LOAD + lane / C::CH;
+    const int pchunk = lane % C::CH;
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int key = key0 + i * C::KEYS_PER_LOAD;
+      koffb[i] = (key * k_sn + (pchunk ^ (key & (C::CH - 1))) * 8) * 2;
+      voffb[i] = (key * v_sn + (pchunk ^ (C::VSW * (key & 3))) * 8) * 2;
+    }
+    // K operand of key block kbk: key 16kbk + s16 (kbk adds an immediate 16
+    // rows: the swizzle depends on the key modulo CH only), logical chunk 4dc + g
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) kro[dc] = s16 * C::ROWB + (((4 * dc + g) ^ (s16 & (C::CH - 1))) * 16);
+    // Vᵀ operand of dim block db, transposing reads: source lane s16 points at
+    // key 4g + s16/4 (+16 for the second read) and dims 16db + 4(s16 mod 4)..+3
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int c = 2 * db + ((s16 & 3) >> 1);
+      vro[db] = (4 * g + (s16 >> 2)) * C::ROWB + ((c ^ (C::VSW * (s16 >> 2))) * 16) + (s16 & 1) * 8;
+    }
+  }
+
+  template <bool IS_V>
+  __device__ __forceinline__ void issue(int buf, const u16 *base, int32_t sn, int pos, int kv) {
+    const u16 *tb = base + (int64_t)pos * sn;
+    const int nrec = ((kv - 1) * sn + D) * 2;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)tb, 0, nrec, kBufferFlags);
+    const int lw = wave - C::FIRST_LOADER;
+    if (lw < 0) return;
+    char *dst = bufp(buf) + (IS_V ? kTileOffV : kTileOffK) + lw * C::LOADS_PER_WAVE * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
+  }
+
+  // Sᵀ blocks (2 key blocks × 3 query blocks) of the K tile in buffer KBUF;
+  // with a fixed reference (FIXED) the chains start from -R (Q pre-scaled).
+  template <int KBUF, bool FIXED>
+  __device__ __forceinline__ void qk(f32x4_t (&sc)[2][kQB]) const {
+    const char *Kb = bufp(KBUF) + kTileOffK;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) sc[kbk][qb] = FIXED ? bias[qb] : f32x4_t{};
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kbk * 16 * C::ROWB);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sc[kbk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], sc[kbk][qb], 0, 0, 0);
+      }
+    // Issue order: two K operand reads ahead of the three MFMAs that use each.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * C::DC - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kQB, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kQB, 1);
+  }
+
+  // keys >= kv of a tile: element r of key block kbk is key 16kbk + 4g + r
+  __device__ __forceinline__ void mask_tail(f32x4_t (&sc)[2][kQB], int kv) {
+    if (kv < C::BN) {
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        const int thr = kv - 16 * kbk - 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r >= thr)
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) sc[kbk][qb][r] = -INFINITY;
+      }
+    }
+  }
+  // A wave whose rows cross the frame boundary, on a key frame only one of
+  // the two frames attends: removes the tile from the rows of the other
+  // frame (bit qb of t1bits: this lane's row of block qb lies in the second
+  // frame; keep_t1: the tile belongs to the second frame's rows).
+  __device__ __forceinline__ void mask_lanes(f32x4_t (&sc)[2][kQB], int t1bits, bool keep_t1) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const bool in_t1 = (t1bits >> qb) & 1;
+      const bool ok = in_t1 == keep_t1;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[kbk][qb][r] = ok ? sc[kbk][qb][r] : -INFINITY;
+    }
+  }
+  // The running max of each query block, raised lazily as in Block::fold_max.
+  __device__ __forceinline__ void fold_max(const f32x4_t (&sc)[2][kQB]) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float mx = sc[0][qb][0];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kbk][qb][r]);
+      mx = row4_max(mx);
+      const float mt = mx * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kMaxLag) != 0) {
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oacc[qb][db][r] *= alpha;
+        m_run[qb] = m_new;
+      }
+    }
+  }
+  // Probabilities, rounded to bf16, as the B operands of P·V (k-slot
+  // 8g + 4kbk + r is key 16kbk + 4g + r); the row sums take the rounded values.
+  template <bool FIXED>
+  __device__ __forceinline__ void probs(const f32x4_t (&sc)[2][kQB], bf16x8_t (&pb)[kQB]) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float neg_m = -m_run[qb];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pb[qb][4 * kbk + r] = (__bf16)__builtin_amdgcn_exp2f(
+              FIXED ? sc[kbk][qb][r] : __builtin_fmaf(sc[kbk][qb][r], scale_log2, neg_m));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pr = {pb[qb][e], pb[qb][e + 1]};
+        l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[qb], false);
+      }
+    }
+  }
+  // Oᵀ += Vᵀ·P with the V tile in buffer VBUF: one pair of transposing
+  // reads per dim block, shared by the three query blocks.
+  template <int VBUF>
+  __device__ __forceinline__ void pv(const bf16x8_t (&pb)[kQB]) {
+    const char *Vb = bufp(VBUF) + kTileOffV;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[db]));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(Vb + vro[db] + 16 * C::ROWB));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        oacc[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qb], oacc[qb][db], 0, 0, 0);
+    }
+    // Issue order: the reads of two dim blocks, then each block's three
+    // MFMAs followed by the next block's reads (measured 4-5% faster than
+    // the compiler's own order, with the K-read order of qk 2-3% more).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+    for (int i = 0; i < C::DB - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kQB, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kQB, 2);
+  }
+  // One key tile from LDS buffer BUF.
+  template <int BUF, bool FIXED>
+  __device__ __forceinline__ void tile(int kv, bool lane_mask, int t1bits, bool keep_t1) {
+    f32x4_t sc[2][kQB];
+    bf16x8_t pb[kQB];
+    qk<BUF, FIXED>(sc);
+    mask_tail(sc, kv);
+    if (lane_mask) mask_lanes(sc, t1bits, keep_t1);
+    if constexpr (!FIXED) fold_max(sc);
+    probs<FIXED>(sc, pb);
+    pv<BUF>(pb);
+  }
+};
+
+// The span kernel: one work item of kSpanRows consecutive query tokens per
+// workgroup (see the top of the file).
+template <int D>
+__global__ __launch_bounds__(SpanCfg<D>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void lvsa_attn_span(Args a) {
+  using C = SpanCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char lds0[C::LDS_BYTES / 2];  // K0 V0
+  __shared__ __attribute__((aligned(1024))) char lds1[C::LDS_BYTES / 2];  // K1 V1
+  SpanBlock<D> blk;
+  blk.lds0 = lds0;
+  blk.lds1 = lds1;
+  const int tid = threadIdx.x;
+  blk.lane = tid & 63;
+  blk.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  blk.s16 = blk.lane & 15;
+  blk.g = blk.lane >> 4;
+  blk.scale_log2 = a.scale_log2;
+
+  int item, half, slot;
+  if (!take_item(a, reinterpret_cast<int *>(lds1), &item, &half, &slot)) return;
+  const Item wi = decode_item<C::BM, true>(a, item);
+  const int P = a.P;
+  const u16 *kbase = a.k + (int64_t)wi.b * a.k_sb + (int64_t)wi.h * a.k_sh;
+  const u16 *vbase = a.v + (int64_t)wi.b * a.v_sb + (int64_t)wi.h * a.v_sh;
+
+  // ---- Q rows: the wave's 48 rows × D as B operands (rows past the item's
+  // end read as zeros and are never stored)
+  const int row0 = wi.tok0 + blk.wave * 16 * kQB;  // token of the wave's first row
+  {
+    const u16 *qh = a.q + (int64_t)wi.b * a.q_sb + (int64_t)wi.h * a.q_sh;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int row = row0 + 16 * qb + blk.s16;
+      const bool ok = row < wi.tok_end;
+      const u16 *qp = qh + (int64_t)(ok ? row : 0) * a.q_sn + blk.g * 8;
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(qp + dc * 32);
+        if (!ok) x = bf16x8_t{};
+        blk.qf[qb][dc] = x;
+      }
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) blk.oacc[qb][db] = f32x4_t{};
+    blk.m_run[qb] = -FLT_MAX;
+    blk.l_run[qb] = 0.f;
+  }
+  blk.init_offsets(a.k_sn, a.v_sn);
+  // Whether the wave has rows in the item (the last item of the sequence may
+  // not fill every wave); which of the walk's frame memberships its rows need
+  // (bit 0: rows in t0, bit 1: rows in t1); and, per lane, which of its
+  // three rows lie in t1.
+  const int compute = __builtin_amdgcn_readfirstlane(row0 < wi.tok_end ? 1 : 0);
+  const bool two = wi.t1 != wi.t0;
+  int need = 3;
+  int t1bits = 0;
+  if (two && compute) {
+    const int f_first = row0 / P;
+    const int f_last = min(row0 + 16 * kQB - 1, wi.tok_end - 1) / P;
+    need = f_first == f_last ? (f_first == wi.t0 ? 1 : 2) : 3;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) t1bits |= ((row0 + 16 * qb + blk.s16) / P == wi.t1 ? 1 : 0) << qb;
+  }
+  need = __builtin_amdgcn_readfirstlane(need);
+
+  // ---- the key walk: the union of the rows of t0 and t1
+  SegIter it = make_walk(a, wi, half);
+  const int n_walk = walk_tiles(it, C::BN);
+
+  // ---- softmax reference, as in the frame kernel, per query row
+  bool fixed = false;
+  if (a.knorm) {
+    const float kn = walk_key_norm(a, wi);
+    float r_ref[kQB];
+    bool all_ok = true;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      float ss = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)(__bf16)((float)blk.qf[qb][dc][e] * a.scale_log2);
+          ss = __builtin_fmaf(x, x, ss);
+        }
+      ss = row4_sum(ss);  // the four lane groups hold a quarter of the row each
+      r_ref[qb] = __builtin_sqrtf(ss) * kn * (1.0f + 1.0f / 256.0f);
+      all_ok = all_ok && (2.0f * r_ref[qb] <= kMaxRefGap);
+    }
+    fixed = __builtin_amdgcn_ballot_w64(!all_ok) == 0;
+    if (fixed) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        blk.m_run[qb] = r_ref[qb];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) blk.bias[qb][r] = -r_ref[qb];
+#pragma unroll
+        for (int dc = 0; dc < C::DC; ++dc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) blk.qf[qb][dc][e] = (__bf16)((float)blk.qf[qb][dc][e] * a.scale_log2);
+      }
+    }
+  }
+
+  // ---- main loop over key tiles, as in the frame kernel.  A tile is
+  // computed by the waves whose rows attend its frame (every wave, unless
+  // the item's rows cross a frame boundary).
+  int pos = 0, kv = 0, mem = 0;
+  auto advance = [&]() {  // next tile, moving to the next segment when needed
+    pos += C::BN;
+    if (pos >= it.ke) {
+      it.next();
+      pos = it.ks;
+    }
+    kv = min(C::BN, it.ke - pos);
+    mem = it.mem;
+  };
+  auto issue = [&](int buf) {
+    blk.template issue<false>(buf, kbase, a.k_sn, pos, kv);
+    blk.template issue<true>(buf, vbase, a.v_sn, pos, kv);
+  };
+  if (n_walk > 0) {
+    it.next();
+    pos = it.ks;
+    kv = min(C::BN, it.ke - pos);
+    mem = it.mem;
+    issue(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  auto run = [&](auto fixed_c) {
+    constexpr bool F = decltype(fixed_c)::value;
+    auto step = [&](auto buf_c, int kvj, int memj) {
+      constexpr int BUF = decltype(buf_c)::value;
+      if (compute && (memj & need)) {
+        // a boundary-crossing wave, on a frame only one of its two frames attends
+        const bool lm = need == 3 && memj != 3;
+        blk.template tile<BUF, F>(kvj, lm, t1bits, memj == 2);
+      }
+    };
+    for (int i = 0; i + 1 < n_walk; i += 2) {
+      const int kv0 = kv, mem0 = mem;
+      advance();  // tile i+1 -> buffer 1
+      issue(1);
+      step(std::integral_constant<int, 0>{}, kv0, mem0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int kv1 = kv, mem1 = mem;
+      if (i + 2 < n_walk) {  // tile i+2 -> buffer 0
+        advance();
+        issue(0);
+      }
+      step(std::integral_constant<int, 1>{}, kv1, mem1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    if (n_walk & 1) step(std::integral_constant<int, 0>{}, kv, mem);
+  };
+  if (fixed)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
+
+  // ---- a half writes its partial record (Oᵀ accumulators; row sums and
+  // references of the three blocks) for lvsa_combine_span
+  if (half >= 0) {
+    if (compute) {
+      constexpr int R4 = kSpanPartialFloats(D) / 4;
+      float4 *rec = reinterpret_cast<float4 *>(a.partial) +
+                    ((int64_t)(slot * 2 + half) * C::NW + blk.wave) * R4 * 64 + blk.lane;
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const f32x4_t o = blk.oacc[qb][db];
+          rec[(qb * C::DB + db) * 64] = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      rec[(kQB * C::DB) * 64] = make_float4(blk.l_run[0], blk.l_run[1], blk.l_run[2], blk.m_run[0]);
+      rec[(kQB * C::DB + 1) * 64] = make_float4(blk.m_run[1], blk.m_run[2], 0.f, 0.f);
+    }
+    return;
+  }
+  // ---- epilogue: normalise, round to bf16, store (each lane: 4 dims of
+  // every 16-dim block of its three rows)
+  {
+    u16 *oh = a.o + (int64_t)wi.b * a.o_sb + (int64_t)wi.h * a.o_sh;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float l_tot = row4_sum(blk.l_run[qb]);  // every lane, before the row test
+      const int row = row0 + 16 * qb + blk.s16;
+      if (row < wi.tok_end) {
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        u16 *op = oh + (int64_t)row * a.o_sn + 4 * blk.g;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          bf16x4_t o4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(blk.oacc[qb][db][r] * inv);
+          *reinterpret_cast<bf16x4_t *>(op + 16 * db) = o4;
+        }
+      }
+    }
+  }
+}
+
+// Merges the two halves of every split item of the span kernel: one
+// workgroup per record slot, one wave per 48 query rows as in
+// lvsa_attn_span (the frame kernel's merge, per query block).
+template <int D>
+__global__ __launch_bounds__(SpanCfg<D>::NW * 64) void lvsa_combine_span(Args a) {
+  using C = SpanCfg<D>;
+  const int x = blockIdx.x / a.split_cap, j = blockIdx.x % a.split_cap;
+  int base, cnt;
+  xcd_range(a.n_wg, x, &base, &cnt);
+  const int S = split_count(a.split_cap, cnt);
+  if (j >= S) return;
+  const Item wi = decode_item<C::BM, true>(a, base + (cnt - S) + j);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s16 = lane & 15, g = lane >> 4;
+  const int row0 = wi.tok0 + wave * 16 * kQB;
+  if (row0 >= wi.tok_end) return;
+  constexpr int R4 = kSpanPartialFloats(D) / 4;
+  const float4 *r0 = reinterpret_cast<const float4 *>(a.partial) + ((int64_t)(blockIdx.x * 2) * C::NW + wave) * R4 * 64 + lane;
+  const float4 *r1 = r0 + (int64_t)C::NW * R4 * 64;
+  const float4 a0 = r0[(kQB * C::DB) * 64], a1 = r1[(kQB * C::DB) * 64];
+  const float4 b0 = r0[(kQB * C::DB + 1) * 64], b1 = r1[(kQB * C::DB + 1) * 64];
+  const float l0[kQB] = {a0.x, a0.y, a0.z}, l1[kQB] = {a1.x, a1.y, a1.z};
+  const float m0[kQB] = {a0.w, b0.x, b0.y}, m1[kQB] = {a1.w, b1.x, b1.y};
+  u16 *oh = a.o + (int64_t)wi.b * a.o_sb + (int64_t)wi.h * a.o_sh;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float m = fmaxf(m0[qb], m1[qb]);
+    const float w0 = __builtin_amdgcn_exp2f(m0[qb] - m);
+    const float w1 = __builtin_amdgcn_exp2f(m1[qb] - m);
+    const float l_tot = row4_sum(w0 * l0[qb] + w1 * l1[qb]);
+    const int row = row0 + 16 * qb + s16;
+    if (row >= wi.tok_end) continue;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    u16 *op = oh + (int64_t)row * a.o_sn + 4 * g;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const float4 o0 = r0[(qb * C::DB + db) * 64], o1 = r1[(qb * C::DB + db) * 64];
+      bf16x4_t o4;
+      o4[0] = (__bf16)((w0 * o0.x + w1 * o1.x) * inv);
+      o4[1] = (__bf16)((w0 * o0.y + w1 * o1.y) * inv);
+      o4[2] = (__bf16)((w0 * o0.z + w1 * o1.z) * inv);
+      o4[3] = (__bf16)((w0 * o0.w + w1 * o1.w) * inv);
+      *reinterpret_cast<bf16x4_t *>(op + 16 * db) = o4;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ host --
@@ -1029,10 +1544,12 @@ bool overlaps(const lvsa_tensor *a, const lvsa_tensor *b) {
   return a0 < b1 && b0 < a1;
 }
 
-template <int D, int NW, bool SPAN>
+// Launches, on one stream: the key-norm pass (with a workspace), the
+// attention kernel ATTN (NT threads per workgroup) and the merge of split
+// items MERGE.
+template <int D, void (*ATTN)(Args), void (*MERGE)(Args), int NT>
 int launch(const Args &args, int n_frames, hipStream_t stream) {
   if (args.knorm) {
-    // the key-norm table first, on the same stream
     hipLaunchKernelGGL((lvsa_key_norms<D>), dim3(n_frames), dim3(256), 0, stream, args.k, args.k_sb, args.k_sh,
                        args.k_sn, args.H, args.T, args.P, const_cast<float *>(args.knorm), args.tickets);
     hipError_t e = hipGetLastError();
@@ -1043,26 +1560,30 @@ int launch(const Args &args, int n_frames, hipStream_t stream) {
   // share of the others' items.
   const int64_t grid =
       args.tickets ? args.n_wg + (int64_t)kNumXcd * args.split_cap + args.n_wg / 8 + kNumXcd : args.n_wg;
-  hipLaunchKernelGGL((lvsa_attn_fwd<D, NW, SPAN>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, args);
+  hipLaunchKernelGGL(ATTN, dim3((unsigned)grid), dim3(NT), 0, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (args.tickets && args.split_cap > 0) {
-    hipLaunchKernelGGL((lvsa_combine<D, NW, SPAN>), dim3(kNumXcd * args.split_cap), dim3(NW * 64), 0, stream, args);
+    hipLaunchKernelGGL(MERGE, dim3(kNumXcd * args.split_cap), dim3(NT), 0, stream, args);
     e = hipGetLastError();
     if (e != hipSuccess) return lvsa::fail(LVSA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
   }
   return lvsa::ok();
 }
+template <int D>
+int launch_frame(const Args &args, int n_frames, hipStream_t stream) {
+  return launch<D, lvsa_attn_frame<D>, lvsa_combine_frame<D>, kFrameWaves * 64>(args, n_frames, stream);
+}
+template <int D>
+int launch_span(const Args &args, int n_frames, hipStream_t stream) {
+  return launch<D, lvsa_attn_span<D>, lvsa_combine_span<D>, SpanCfg<D>::NW * 64>(args, n_frames, stream);
+}
 
 // How a call is cut into work items.  Frames of at least kSpanRows tokens
-// (every video workload) use 12-wave workgroups of kSpanRows consecutive
-// tokens, which may cross one frame boundary; one such workgroup fills a
-// CU (3 waves per SIMD) and loads each K/V tile once for three times the
-// rows of a 4-wave one.  Shorter frames use 4-wave workgroups of 128 rows
-// of one frame.
-constexpr int kSpanWaves = 12;
-constexpr int kSpanRows = kSpanWaves * 32;
-constexpr int kFrameWaves = 4;
+// (every video workload): items of kSpanRows consecutive tokens, which may
+// cross one frame boundary, for 8-wave workgroups of the span kernel (one
+// per CU).  Shorter frames: items of 128 rows of one frame for 4-wave
+// workgroups of the frame kernel.
 struct Plan {
   bool span;
   int nw, q_tiles;
@@ -1074,10 +1595,10 @@ Plan plan_for(int64_t B, int64_t H, int64_t N, int64_t T) {
   const int64_t P = N / T;
   p.span = P >= kSpanRows;
   if (p.span) {
-    p.nw = kSpanWaves;
+    p.nw = SpanCfg<128>::NW;
     p.q_tiles = (int)((N + kSpanRows - 1) / kSpanRows);
     p.items = B * H * p.q_tiles;
-    p.split_per_xcd = 32;  // 16-128 measured within 0.8% of each other; 32 best or tied
+    p.split_per_xcd = 32;
   } else {
     p.nw = kFrameWaves;
     p.q_tiles = (int)((P + kFrameWaves * 32 - 1) / (kFrameWaves * 32));
@@ -1090,7 +1611,7 @@ Plan plan_for(int64_t B, int64_t H, int64_t N, int64_t T) {
 // Workspace: the key-norm table (B·H·T floats), then, at the next
 // 256-byte boundary, the 8 ticket counters (256 bytes), then the partial
 // records of the split items (8·split_cap slots × 2 halves × NW waves × 64
-// lanes × kPartialFloats(D) floats).
+// lanes × kSpanPartialFloats(D) or kPartialFloats(D) floats).
 int64_t norms_bytes_for(int64_t B, int64_t H, int64_t T) {
   return ((B * H * T * (int64_t)sizeof(float) + 255) / 256) * 256;
 }
@@ -1100,6 +1621,7 @@ int32_t split_cap_for(const Plan &p) {
 }
 // Bytes of partial records per unit of split_cap (one slot per XCD).
 int64_t split_unit_bytes(const Plan &p, int64_t D) {
+  if (p.span) return (int64_t)kNumXcd * 2 * p.nw * 64 * kSpanPartialFloats((int)D) * 4;
   return (int64_t)kNumXcd * 2 * p.nw * 64 * kPartialFloats((int)D) * 4;
 }
 int64_t workspace_bytes_for(int64_t B, int64_t H, int64_t N, int64_t D, int64_t T, int32_t split_cap) {
@@ -1193,11 +1715,11 @@ int attention_impl(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n_frames = (int)(q->B * q->H * T);
   if (plan.span) {
-    if (D == 128) return launch<128, kSpanWaves, true>(a, n_frames, s);
-    return launch<64, kSpanWaves, true>(a, n_frames, s);
+    if (D == 128) return launch_span<128>(a, n_frames, s);
+    return launch_span<64>(a, n_frames, s);
   }
-  if (D == 128) return launch<128, kFrameWaves, false>(a, n_frames, s);
-  return launch<64, kFrameWaves, false>(a, n_frames, s);
+  if (D == 128) return launch_frame<128>(a, n_frames, s);
+  return launch_frame<64>(a, n_frames, s);
 }
 
 }  // namespace

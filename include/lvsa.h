@@ -205,19 +205,20 @@ int lvsa_attention(const lvsa_tensor *q, const lvsa_tensor *k, const lvsa_tensor
  * pages define no workspace): one float per (b, h, frame) rounded up to
  * 256, 256 bytes of work counters, and room for the partial results of the
  * work items that run as two halves (see lvsa_attention_ws: at most 32 per
- * XCD of 12-wave records when frames hold >= 384 tokens, 96 of 4-wave
- * records otherwise; about 107 MB at D = 128 once there are enough items,
+ * XCD of 8-wave records when frames hold >= 384 tokens, 96 of 4-wave
+ * records otherwise; about 109 MB at D = 128 once there are enough items,
  * none below 32 items).
  * Errors: LVSA_ERR_ARG, LVSA_ERR_SHAPE (D not 64/128, N % T != 0). */
 int lvsa_attention_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int32_t T, int64_t *bytes);
 
 /* Work items (both attention entry points).  Frames of at least 384 tokens
  * (every video workload): items of 384 consecutive query tokens of one
- * (b, h), run by 12-wave workgroups, one per CU; an item that crosses a
- * frame boundary walks the union of the two frames' rows, each wave (or,
- * for a wave whose 32 rows straddle the boundary, each row) taking only its
- * own frame's key frames.  Shorter frames: items of 128 rows of one frame,
- * 4-wave workgroups.  Items are cut into 8 contiguous ranges, one per XCD.
+ * (b, h), run by 8-wave workgroups of 48 rows per wave, one per CU; an item
+ * that crosses a frame boundary walks the union of the two frames' rows,
+ * each wave (or, for a wave whose rows straddle the boundary, each row)
+ * taking only its own frame's key frames.  Shorter frames: items of 128
+ * rows of one frame, 4-wave workgroups.  Items are cut into 8 contiguous
+ * ranges, one per XCD.
  *
  * lvsa_attention with a caller-provided device workspace (a library
  * convention: the pages define the computation, not this split of it),

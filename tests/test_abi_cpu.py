@@ -186,12 +186,16 @@ def test_attention_rejects_bad_arguments_before_any_device_work():
 
 def test_workspace_bytes():
     # key norms: B*H*T frames x 1 float, rounded up to 256 bytes; 256 bytes
-    # of counters; then the partial records of the split items: 8 XCD ranges
-    # x min(96, items / 32) items x 2 halves x 4 waves x 64 lanes x (D/2 + 4)
-    # floats, items = B*H*T*ceil(P/128)
-    rec = 8 * 96 * 2 * 4 * 64 * 68 * 4
+    # of counters; then the partial records of the split items.  Frames of
+    # >= 384 tokens: 8 XCD ranges x min(32, items / 32) items x 2 halves x 8
+    # waves x 64 lanes x (3 D/4 + 8) floats, items = B*H*ceil(N/384).
+    # Shorter frames: 8 x min(96, items / 32) x 2 x 4 waves x 64 lanes x
+    # (D/2 + 4) floats, items = B*H*T*ceil(P/128).
+    rec = 8 * 32 * 2 * 8 * 64 * 104 * 4
     assert L.lvsa_attention_workspace_bytes(1, 12, 121 * 1560, 128, 121) == 5888 + 256 + rec
     assert L.lvsa_attention_workspace_bytes(2, 40, 121 * 1560, 128, 121) == 38912 + 256 + rec
+    # 1 x 2 x ceil(20 * 400 / 384) = 42 items: 1 per XCD range, 3 D/4 + 8 = 56 floats at D = 64
+    assert L.lvsa_attention_workspace_bytes(1, 2, 20 * 400, 64, 20) == 256 + 256 + 8 * 1 * 2 * 8 * 64 * 56 * 4
     assert L.lvsa_attention_workspace_bytes(1, 2, 8 * 64, 64, 8) == 512  # 16 items: nothing split
     # 1 x 4 x 40 frames x 1 tile = 160 items: 5 per XCD range, (D/2 + 4) = 36 floats
     assert L.lvsa_attention_workspace_bytes(1, 4, 40 * 100, 64, 40) == 768 + 256 + 8 * 5 * 2 * 4 * 64 * 36 * 4

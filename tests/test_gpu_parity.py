@@ -88,8 +88,8 @@ MID_CASES = [
     (2, 2, 7, 129, 64, 7, 3, 105),     # C = T: dense, one run of 903 keys; 1-row last tile
     (1, 1, 1, 300, 128, 4, 2, 106),    # a single frame
     (1, 3, 20, 64, 128, 9, 4, 107),    # key tiles exactly aligned to frames
-    # frames of >= 384 tokens: 12-wave items of 384 consecutive tokens, which
-    # cross frame boundaries and walk the union of two frames' rows
+    # frames of >= 384 tokens: items of 384 consecutive tokens (8 waves of 48
+    # rows), which cross frame boundaries and walk the union of two frames' rows
     (1, 2, 7, 400, 128, 4, 2, 108),    # nearly every item crosses a boundary (inside a wave)
     (2, 1, 5, 384, 64, 3, 1, 109),     # items aligned to frames: none crosses
     (1, 3, 6, 1000, 64, 4, 2, 110),    # d = 64, a boundary inside a wave
