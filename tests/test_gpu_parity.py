@@ -600,11 +600,13 @@ def split_layout(B, H, T, P):
 
 
 def item_rows(tok0, tok_end):
-    """The first and last row of each wave of a work item, as tokens."""
+    """Edge rows of a work item of 384 tokens, as tokens: each 48-row wave's
+    first and last row and the first row of its second and third 16-row
+    query block."""
     rows = set()
-    for w0 in range(tok0, tok_end, 32):
-        rows.add(w0)
-        rows.add(min(w0 + 31, tok_end - 1))
+    for w0 in range(tok0, tok_end, 48):
+        for r in (w0, w0 + 16, w0 + 32, w0 + 47):
+            rows.add(min(r, tok_end - 1))
     return rows
 
 
