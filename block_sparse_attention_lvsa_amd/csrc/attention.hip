@@ -1109,6 +1109,10 @@ struct SpanBlock {
     }
   }
   // The running max of each query block, raised lazily as in Block::fold_max.
+  // Whether any row's tile max exceeds its reference by more than kMaxLag is
+  // decided on each lane's part of the row (the scaled maximum is the maximum
+  // of the scaled parts), so the reduction over the row's four lanes runs
+  // only when a rescale follows.
   __device__ __forceinline__ void fold_max(const f32x4_t (&sc)[2][kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -1117,9 +1121,8 @@ struct SpanBlock {
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kbk][qb][r]);
-      mx = row4_max(mx);
-      const float mt = mx * scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kMaxLag) != 0) {
+      if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > m_run[qb] + kMaxLag) != 0) {
+        const float mt = row4_max(mx) * scale_log2;
         const float m_new = fmaxf(m_run[qb], mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
 #pragma unroll
