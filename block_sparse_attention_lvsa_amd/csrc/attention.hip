@@ -1079,7 +1079,7 @@ struct SpanBlock {
 
   // keys >= kv of a tile: element r of key block kbk is key 16kbk + 4g + r
   __device__ __forceinline__ void mask_tail(f32x4_t (&sc)[2][kQB], int kv) {
-    if (kv < C::BN) {
+    if (__builtin_expect(kv < C::BN, 0)) {
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
@@ -1188,7 +1188,7 @@ struct SpanBlock {
     bf16x8_t pb[kQB];
     qk<BUF, FIXED>(sc);
     mask_tail(sc, kv);
-    if (lane_mask) mask_lanes(sc, t1bits, keep_t1);
+    if (__builtin_expect(lane_mask, 0)) mask_lanes(sc, t1bits, keep_t1);
     if constexpr (!FIXED) fold_max(sc);
     probs<FIXED>(sc, pb);
     pv<BUF>(pb);
@@ -1308,7 +1308,7 @@ void lvsa_attn_span(Args a) {
   int pos = 0, kv = 0, mem = 0;
   auto advance = [&]() {  // next tile, moving to the next segment when needed
     pos += C::BN;
-    if (pos >= it.ke) {
+    if (__builtin_expect(pos >= it.ke, 0)) {
       it.next();
       pos = it.ks;
     }
@@ -1332,7 +1332,7 @@ void lvsa_attn_span(Args a) {
     constexpr bool F = decltype(fixed_c)::value;
     auto step = [&](auto buf_c, int kvj, int memj) {
       constexpr int BUF = decltype(buf_c)::value;
-      if (compute && (memj & need)) {
+      if (__builtin_expect(compute && (memj & need), 1)) {
         // a boundary-crossing wave, on a frame only one of its two frames attends
         const bool lm = need == 3 && memj != 3;
         blk.template tile<BUF, F>(kvj, lm, t1bits, memj == 2);
