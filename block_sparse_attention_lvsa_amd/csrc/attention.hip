@@ -1049,10 +1049,18 @@ struct SpanBlock {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + i * 1024), 16, IS_V ? voffb[i] : koffb[i], 0, 0, 0);
   }
 
+  // The first K operand reads of a tile (reduction step 0, both key blocks),
+  // issued right after the barrier, ahead of the walk's scalar work.
+  template <int KBUF>
+  __device__ __forceinline__ void kpre(bf16x8_t (&kp)[2]) const {
+    const char *Kb = bufp(KBUF) + kTileOffK;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) kp[kbk] = *(const lds_bf16x8 *)(Kb + kro[0] + kbk * 16 * C::ROWB);
+  }
   // Sᵀ blocks (2 key blocks × 3 query blocks) of the K tile in buffer KBUF;
   // with a fixed reference (FIXED) the chains start from -R (Q pre-scaled).
   template <int KBUF, bool FIXED>
-  __device__ __forceinline__ void qk(f32x4_t (&sc)[2][kQB]) const {
+  __device__ __forceinline__ void qk(f32x4_t (&sc)[2][kQB], const bf16x8_t (&kp)[2]) const {
     const char *Kb = bufp(KBUF) + kTileOffK;
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk)
@@ -1062,13 +1070,12 @@ struct SpanBlock {
     for (int dc = 0; dc < C::DC; ++dc)
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
-        const bf16x8_t kf = *(const lds_bf16x8 *)(Kb + kro[dc] + kbk * 16 * C::ROWB);
+        const bf16x8_t kf = dc == 0 ? kp[kbk] : *(const lds_bf16x8 *)(Kb + kro[dc] + kbk * 16 * C::ROWB);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           sc[kbk][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][dc], sc[kbk][qb], 0, 0, 0);
       }
-    // Issue order: two K operand reads ahead of the three MFMAs that use each.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    // Issue order: each later K operand read two MFMA groups ahead of its use.
 #pragma unroll
     for (int i = 0; i < 2 * C::DC - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, kQB, 1);
@@ -1183,10 +1190,10 @@ struct SpanBlock {
   }
   // One key tile from LDS buffer BUF.
   template <int BUF, bool FIXED>
-  __device__ __forceinline__ void tile(int kv, bool lane_mask, int t1bits, bool keep_t1) {
+  __device__ __forceinline__ void tile(int kv, bool lane_mask, int t1bits, bool keep_t1, const bf16x8_t (&kp)[2]) {
     f32x4_t sc[2][kQB];
     bf16x8_t pb[kQB];
-    qk<BUF, FIXED>(sc);
+    qk<BUF, FIXED>(sc, kp);
     mask_tail(sc, kv);
     if (__builtin_expect(lane_mask, 0)) mask_lanes(sc, t1bits, keep_t1);
     if constexpr (!FIXED) fold_max(sc);
@@ -1330,31 +1337,37 @@ void lvsa_attn_span(Args a) {
   __syncthreads();
   auto run = [&](auto fixed_c) {
     constexpr bool F = decltype(fixed_c)::value;
-    auto step = [&](auto buf_c, int kvj, int memj) {
+    auto step = [&](auto buf_c, int kvj, int memj, const bf16x8_t (&kp)[2]) {
       constexpr int BUF = decltype(buf_c)::value;
       if (__builtin_expect(compute && (memj & need), 1)) {
         // a boundary-crossing wave, on a frame only one of its two frames attends
         const bool lm = need == 3 && memj != 3;
-        blk.template tile<BUF, F>(kvj, lm, t1bits, memj == 2);
+        blk.template tile<BUF, F>(kvj, lm, t1bits, memj == 2, kp);
       }
     };
+    bf16x8_t kp[2];
     for (int i = 0; i + 1 < n_walk; i += 2) {
       const int kv0 = kv, mem0 = mem;
+      blk.template kpre<0>(kp);
       advance();  // tile i+1 -> buffer 1
       issue(1);
-      step(std::integral_constant<int, 0>{}, kv0, mem0);
+      step(std::integral_constant<int, 0>{}, kv0, mem0, kp);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       const int kv1 = kv, mem1 = mem;
+      blk.template kpre<1>(kp);
       if (i + 2 < n_walk) {  // tile i+2 -> buffer 0
         advance();
         issue(0);
       }
-      step(std::integral_constant<int, 1>{}, kv1, mem1);
+      step(std::integral_constant<int, 1>{}, kv1, mem1, kp);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    if (n_walk & 1) step(std::integral_constant<int, 0>{}, kv, mem);
+    if (n_walk & 1) {
+      blk.template kpre<0>(kp);
+      step(std::integral_constant<int, 0>{}, kv, mem, kp);
+    }
   };
   if (fixed)
     run(std::true_type{});
